@@ -1,0 +1,116 @@
+"""Pins of the reference planner (oracle.plan): a hand-worked plan, LPT properties,
+Graham's bound against brute-force optimal makespans, and hand-worked automatic
+tile sizes. CPU only."""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import plan as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def check_invariants(seq_lens, Hkv, T, W, p):
+    items = p["items"]
+    B = len(seq_lens)
+    nb = [(int(L) + T - 1) // T for L in seq_lens]
+    assert list(p["req_tile_base"]) == list(np.concatenate([[0], np.cumsum(nb)]))
+    seen = {(int(b), int(g), int(i)) for b, g, i, _ in items}
+    assert len(seen) == len(items) == Hkv * sum(nb)
+    assert seen == {(b, g, i) for b in range(B) for g in range(Hkv) for i in range(nb[b])}
+    slots = sorted(int(s) for *_, s in items)
+    assert slots == list(range(len(items)))
+    for b, g, i, s in items:
+        assert s == Hkv * p["req_tile_base"][b] + g * nb[b] + i
+    assert p["worker_offsets"][0] == 0 and p["worker_offsets"][-1] == len(items)
+    assert (np.diff(p["worker_offsets"]) >= 0).all()
+    loads = np.zeros(W, dtype=np.int64)
+    for w in range(W):
+        for b, g, i, _ in items[p["worker_offsets"][w]:p["worker_offsets"][w + 1]]:
+            loads[w] += min(seq_lens[b], (i + 1) * T) - i * T
+    assert np.array_equal(loads, p["loads"])
+    assert loads.sum() == Hkv * sum(int(x) for x in seq_lens)
+    assert loads.max() - loads.min() <= T
+
+
+def test_hand_worked_plan():
+    with open(os.path.join(GOLDEN, "plan_small.json")) as f:
+        g = json.load(f)
+    p = P.lpt_plan(g["seq_lens"], g["num_kv_heads"], g["tile_tokens"], g["num_workers"])
+    assert p["items"].tolist() == g["items"]
+    assert p["worker_offsets"].tolist() == g["worker_offsets"]
+    assert p["req_tile_base"].tolist() == g["req_tile_base"]
+
+
+def test_equal_costs_are_round_robin():
+    p = P.lpt_plan([64, 128, 32], 3, 32, 5)
+    order = []
+    # LPT order of equal-cost items is (b, g, i) ascending; item k goes to worker k mod W
+    keys = sorted((b, g, i) for b, L in enumerate([64, 128, 32]) for g in range(3) for i in range(L // 32))
+    for k, key in enumerate(keys):
+        w = k % 5
+        lst = [tuple(x[:3]) for x in p["items"][p["worker_offsets"][w]:p["worker_offsets"][w + 1]]]
+        assert key in lst
+        order.append(key)
+    check_invariants([64, 128, 32], 3, 32, 5, p)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(1, 300), min_size=1, max_size=6), st.integers(1, 3),
+       st.sampled_from([16, 32, 48, 64]), st.integers(1, 9))
+def test_invariants_random(seq_lens, Hkv, T, W):
+    check_invariants(seq_lens, Hkv, T, W, P.lpt_plan(seq_lens, Hkv, T, W))
+
+
+def brute_force_opt(costs, W):
+    best = None
+    for assign in itertools.product(range(W), repeat=len(costs)):
+        loads = [0] * W
+        for c, w in zip(costs, assign):
+            loads[w] += c
+        m = max(loads)
+        best = m if best is None else min(best, m)
+    return best
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.integers(1, 64), min_size=1, max_size=4), st.integers(1, 3))
+def test_graham_lpt_bound(seq_lens, W):
+    T = 16
+    p = P.lpt_plan(seq_lens, 1, T, W)
+    costs = [min(L, (i + 1) * T) - i * T for L in seq_lens for i in range((L + T - 1) // T)]
+    if len(costs) > 8:
+        return
+    opt = brute_force_opt(costs, W)
+    assert 3 * W * int(p["loads"].max()) <= (4 * W - 1) * opt
+
+
+def test_auto_tile_hand_worked():
+    # one request of 64 tokens, D=64, bf16, M=1, W=4: T=16 gives makespan 16 and
+    # one item per worker: 16*2*64*2 + (1+1)*1*65*4 = 4616; T=32: 8192 + 520;
+    # T>=64: 16384 + 520. So T=16.
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4) == 16
+    # W=1: T=16 -> 16384 + (4+4)*260; T=32 -> 16384 + (2+2)*260; T>=64 -> 16384 + 2*260
+    # for every T from 64 to 4096 (a tie), so the largest candidate wins.
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 1) == 4096
+    # fp8 with page 16: the quantum is lcm(16, 64) = 64
+    assert P.tile_quantum(16, "fp8") == 64 and P.tile_quantum(64, "fp8") == 64
+    assert P.tile_quantum(32, "bf16") == 32
+
+
+@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 4096, 512), ("mixed", 2048, 4256),
+                                      ("long", 2048, 512), ("fp8_spec", 512, 4712)])
+def test_auto_tile_on_workloads(name, T, N):
+    import synth
+    cfg = synth.ALL[name]
+    sl = synth.draw_seq_lens(cfg, np.random.default_rng(0))
+    t = P.auto_tile_tokens(sl, cfg["q_len"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"],
+                           cfg["page_size"], cfg["kv_format"], 512)
+    assert t == T
+    p = P.lpt_plan(sl, cfg["num_kv_heads"], t, 512)
+    assert len(p["items"]) == N
