@@ -1,0 +1,178 @@
+/*
+ * pkv.h - C ABI of libpkv.so: paged-KV grouped-query decode attention with
+ * split-KV parallelism for AMD Instinct MI355X (gfx950).
+ *
+ * The method (HALOps README, "Highlights"; HPC-Ops review, section "How the kernels
+ * are organized around specific workload shapes"): decode attention over a paged
+ * KV cache with grouped-query heads, BF16 or FP8 KV and a few speculative query
+ * tokens; before every decode step each request's KV is cut into uniform tiles
+ * that greedy bin-packing spreads over the workers; a split-KV kernel computes one
+ * softmax-normalised partial result per tile, and a combine kernel merges them.
+ *
+ * One decode step through this ABI:
+ *   1. pkv_plan_query + pkv_plan   (host; builds the work list from seq_lens)
+ *   2. copy items / worker_offsets / req_tile_base to the device (caller)
+ *   3. pkv_decode_partial          (enqueued on a HIP stream)
+ *   4. pkv_combine                 (enqueued on the same stream)
+ *
+ * Conventions
+ * - Every buffer, host or device, is allocated and owned by the caller. The
+ *   library allocates nothing, keeps no state between calls and is thread-safe;
+ *   the only per-thread state is the message behind pkv_last_error().
+ * - Functions return a pkv_status (0 = success). Nothing aborts or throws across
+ *   the ABI. Device entry points validate their host-visible arguments before any
+ *   HIP call, then enqueue asynchronously and return without synchronising.
+ * - Symbols used below: B = requests, Tq = query tokens per request (q_len),
+ *   Hq / Hkv = query / kv heads, G = Hq / Hkv, M = G * Tq rows per work item,
+ *   D = head_dim, P = page_size, T = tile tokens, W = workers.
+ * - Layouts (row-major, last index fastest):
+ *     q            bf16 [B, Tq, Hq, D]
+ *     k/v_cache    bf16 or OCP e4m3fn bytes [num_pages, Hkv, P, D]
+ *     k/v_scale    fp32 [num_pages, Hkv]: one scale per physical page and kv head
+ *     block_table  int32 [B, bt_stride]; entry (b, p) is the physical page of
+ *                  request b's logical page p; only p < ceil(L_b / P) is read
+ *     seq_lens     int32 [B]; L_b counts the Tq draft tokens, which sit at
+ *                  positions L_b - Tq .. L_b - 1; draft row t sees keys 0 .. L_b-Tq+t
+ *     out          bf16 [B, Tq, Hq, D]; lse_out fp32 [B, Tq, Hq] (natural log)
+ *   Query head h reads kv head h / G. Tokens at or past L_b in a request's last
+ *   page, block-table padding and unreferenced pages are never read.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* KV element formats. FP8 is OCP e4m3fn (bias 7, max 448, no infinities). */
+enum pkv_kv_format { PKV_KV_BF16 = 0, PKV_KV_FP8_E4M3FN = 1 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum, ... */
+  PKV_ERR_UNSUPPORTED = -2,  /* D not 64/128; P not a multiple of 16; fp8 with P != 64;
+                                Hq % Hkv != 0; Tq not in [1, 4]; M > 16; tile not a
+                                multiple of the quantum */
+  PKV_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
+  PKV_ERR_WORKSPACE = -4,    /* workspace smaller than pkv_workspace_bytes() */
+  PKV_ERR_HIP = -5,          /* HIP runtime error; detail in pkv_last_error() */
+  PKV_ERR_SEQ = -6           /* some L_b < 1 or L_b < Tq */
+};
+
+/* Version of this ABI (PKV_ABI_VERSION of the built library). */
+int pkv_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* pkv_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none); the pointer is
+ * valid until the next failing call on that thread. */
+const char* pkv_last_error(void);
+
+/*
+ * Resolve the tile size and the plan's sizes for one decode step (host only).
+ *
+ * seq_lens_h : host int32 [batch]. tile_tokens: T, a multiple of the quantum
+ * (P for bf16, lcm(P, 64) for fp8), or 0 for the automatic choice: among
+ * quantum * 2^k <= 4096 the T minimising
+ *   makespan_tokens(T) * 2 * D * eb + (max_items_per_worker(T) + ceil(N(T) / W)) * M * (D + 1) * 4
+ * (eb = bytes per KV element), ties going to the larger T. num_workers: W >= 1
+ * (see pkv_default_num_workers). Outputs: the resolved T, N = number of work
+ * items, and the number of partial slots (= N).
+ * Errors: INVALID_ARG (null pointer, batch < 0, W < 1), UNSUPPORTED (shape
+ * rules above), SEQ (some L_b < max(1, q_len)).
+ */
+int pkv_plan_query(int batch, const int32_t* seq_lens_h, int q_len, int num_q_heads,
+                   int num_kv_heads, int head_dim, int page_size, int kv_format,
+                   int tile_tokens, int num_workers, int32_t* tile_tokens_out,
+                   int64_t* num_items_out, int64_t* num_partials_out);
+
+/*
+ * Build the work list for tile size T and W workers (host only, deterministic).
+ *
+ * Work item (b, g, i) covers kv head g of request b, tokens [i*T, min(L_b, (i+1)*T)),
+ * i < n_b = ceil(L_b / T); its cost is its token count. Items are placed longest
+ * first (ties by (b, g, i) ascending), each on the least-loaded worker (ties to
+ * the lowest index) - the greedy bin-packing of the HPC-Ops review.
+ * Outputs (caller-allocated host arrays):
+ *   items_h          int32 [N][4] = (b, g, i, slot), grouped by worker, each
+ *                    worker's items in assignment order;
+ *                    slot = Hkv * req_tile_base[b] + g * n_b + i
+ *   worker_offsets_h int32 [W + 1]: worker w owns items [offsets[w], offsets[w+1])
+ *   req_tile_base_h  int32 [batch + 1]: prefix sums of n_b
+ * Errors: INVALID_ARG, SEQ (as pkv_plan_query).
+ */
+int pkv_plan(int batch, const int32_t* seq_lens_h, int q_len, int num_kv_heads,
+             int tile_tokens, int num_workers, int32_t* items_h,
+             int32_t* worker_offsets_h, int32_t* req_tile_base_h);
+
+/* Recommended W for a device: compute units x resident decode workgroups per unit.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP (no such device). */
+int pkv_default_num_workers(int device, int kv_format, int head_dim, int* out);
+
+/* Workspace bytes for num_partials partial results of rows_per_partial (= M) rows
+ * of D fp32 values plus one fp32 log-sum-exp per row; layout: o block at offset
+ * 0, lse block at the next 256-byte boundary. Errors: INVALID_ARG. */
+int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim,
+                        size_t* out);
+
+/* Arguments of pkv_decode_partial. Device pointers unless noted. */
+typedef struct pkv_decode_args {
+  size_t struct_size;             /* sizeof(pkv_decode_args) */
+  const void* q;                  /* bf16 [B, Tq, Hq, D] */
+  const void* k_cache;            /* [num_pages, Hkv, P, D], bf16 or e4m3fn */
+  const void* v_cache;            /* same layout as k_cache */
+  const float* k_scale;           /* fp32 [num_pages, Hkv]; NULL iff bf16 */
+  const float* v_scale;           /* fp32 [num_pages, Hkv]; NULL iff bf16 */
+  const int32_t* block_table;     /* int32 [B, bt_stride] */
+  const int32_t* seq_lens;        /* int32 [B]; must equal the plan's seq_lens_h */
+  const int32_t* items;           /* int32 [num_items][4] from pkv_plan */
+  const int32_t* worker_offsets;  /* int32 [num_workers + 1] from pkv_plan */
+  const int32_t* req_tile_base;   /* int32 [B + 1] from pkv_plan */
+  void* workspace;                /* pkv_workspace_bytes(num_partials, M, D) bytes */
+  size_t workspace_bytes;
+  int64_t num_items;
+  int64_t num_partials;
+  int64_t num_pages;
+  int batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride;
+  int kv_format;                  /* enum pkv_kv_format */
+  int tile_tokens;                /* resolved T of the plan */
+  int num_workers;                /* W of the plan */
+  float scale;                    /* softmax scale applied to q.k (e.g. 1/sqrt(D)) */
+} pkv_decode_args;
+
+/*
+ * Split-KV partial attention: one persistent workgroup per worker walks its
+ * items; for item (b, g, i) it gathers the tile's K/V pages through the block
+ * table, runs an online softmax over the tile and writes, for each of the M rows
+ * r = t*G + j (query token t, head g*G + j), the normalised partial output o
+ * (fp32 [D]) and its log-sum-exp (fp32, natural log; -inf with o = 0 when the
+ * causal mask hides every key of the tile from that row) into slot `slot`.
+ * `stream` is a hipStream_t (NULL = null stream). Enqueue only; no sync.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (q, caches, workspace must be
+ * 16-byte aligned), WORKSPACE, HIP (launch failure).
+ */
+int pkv_decode_partial(const pkv_decode_args* args, void* stream);
+
+/*
+ * Log-sum-exp merge of the partials of each row (b, t, h):
+ *   M* = max_i lse_i, w_i = exp(lse_i - M*), out = sum_i w_i o_i / sum_i w_i,
+ *   lse_out = M* + ln sum_i w_i,   i = 0 .. n_b - 1 in order (deterministic),
+ * n_b = req_tile_base[b+1] - req_tile_base[b] (device array). out is written in
+ * bf16 (round to nearest even); lse_out may be NULL. Same workspace and stream as
+ * pkv_decode_partial. Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP.
+ */
+int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_partials,
+                const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
+                int num_kv_heads, int head_dim, void* out, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,327 @@
+"""Python binding of libpkv.so: paged-KV GQA split-KV decode attention on MI355X.
+
+Thin ctypes wrappers with the C ABI's names (argument marshalling only; every step
+of the decode path runs in the library), plus ``PagedDecode``, a per-step runner
+that plans on the host, uploads the plan on the caller's stream and enqueues the
+two kernels. PyTorch supplies device memory and streams.
+
+The library is built in-tree (``python -m paged_kv_gqa_amd._build``); importing
+this package without it raises ImportError - there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+KV_BF16 = 0
+KV_FP8_E4M3FN = 1
+KV_FORMATS = {"bf16": KV_BF16, "fp8": KV_FP8_E4M3FN}
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_ALIGNMENT = -3
+PKV_ERR_WORKSPACE = -4
+PKV_ERR_HIP = -5
+PKV_ERR_SEQ = -6
+
+MAX_ROWS = 16  # largest (q heads per kv head) x (query tokens) per work item
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, func, detail):
+        super().__init__("%s failed: %s (%d): %s" % (func, _status_text(status), status, detail))
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``pkv_decode_args`` (include/pkv.h)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("items", ctypes.c_void_p), ("worker_offsets", ctypes.c_void_p),
+        ("req_tile_base", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_items", ctypes.c_int64), ("num_partials", ctypes.c_int64),
+        ("num_pages", ctypes.c_int64),
+        ("batch", ctypes.c_int), ("q_len", ctypes.c_int), ("num_q_heads", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("tile_tokens", ctypes.c_int),
+        ("num_workers", ctypes.c_int), ("scale", ctypes.c_float),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpkv.so is not built (expected at %s); run "
+                          "`python -m paged_kv_gqa_amd._build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "pkv_abi_version": (ctypes.c_int, []),
+        "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_plan_query": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, _i32p, _i64p, _i64p]),
+        "pkv_plan": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, _i32p, _i32p, _i32p]),
+        "pkv_default_num_workers": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_int)]),
+        "pkv_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_size_t)]),
+        "pkv_decode_partial": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
+        "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _status_text(status):
+    return _lib.pkv_status_string(status).decode()
+
+
+def _check(status, func):
+    if status != PKV_OK:
+        raise PkvError(status, func, _lib.pkv_last_error().decode())
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+def _ptr(t):
+    """Address of a torch tensor / numpy array / int / None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------------
+# C ABI, one wrapper per entry point
+
+
+def pkv_abi_version():
+    return _lib.pkv_abi_version()
+
+
+def pkv_status_string(status):
+    return _status_text(status)
+
+
+def pkv_last_error():
+    return _lib.pkv_last_error().decode()
+
+
+def pkv_plan_query(seq_lens_h, q_len, num_q_heads, num_kv_heads, head_dim, page_size, kv_format,
+                   tile_tokens, num_workers):
+    """Returns (tile_tokens, num_items, num_partials)."""
+    sl, slp = _i32(seq_lens_h)
+    T = ctypes.c_int32()
+    N = ctypes.c_int64()
+    NP = ctypes.c_int64()
+    _check(_lib.pkv_plan_query(len(sl), slp, q_len, num_q_heads, num_kv_heads, head_dim, page_size,
+                               KV_FORMATS.get(kv_format, kv_format), tile_tokens, num_workers,
+                               ctypes.byref(T), ctypes.byref(N), ctypes.byref(NP)), "pkv_plan_query")
+    return T.value, N.value, NP.value
+
+
+def pkv_plan(seq_lens_h, q_len, num_kv_heads, tile_tokens, num_workers, num_items=None, out=None):
+    """Build the plan. Returns (items [N,4], worker_offsets [W+1], req_tile_base [B+1]) as
+    int32 numpy arrays; with ``out`` = (items, offsets, rtb) writes into those arrays."""
+    sl, slp = _i32(seq_lens_h)
+    B = len(sl)
+    if out is None:
+        if num_items is None:
+            num_items = sum((int(L) + tile_tokens - 1) // tile_tokens for L in sl) * num_kv_heads
+        out = (np.empty((num_items, 4), np.int32), np.empty(num_workers + 1, np.int32),
+               np.empty(B + 1, np.int32))
+    items, offs, rtb = out
+    for a in out:
+        assert a.dtype == np.int32 and a.flags.c_contiguous
+    _check(_lib.pkv_plan(B, slp, q_len, num_kv_heads, tile_tokens, num_workers,
+                         items.ctypes.data_as(_i32p), offs.ctypes.data_as(_i32p),
+                         rtb.ctypes.data_as(_i32p)), "pkv_plan")
+    return items, offs, rtb
+
+
+def pkv_default_num_workers(device=0, kv_format="bf16", head_dim=128):
+    out = ctypes.c_int()
+    _check(_lib.pkv_default_num_workers(device, KV_FORMATS.get(kv_format, kv_format), head_dim,
+                                        ctypes.byref(out)), "pkv_default_num_workers")
+    return out.value
+
+
+def pkv_workspace_bytes(num_partials, rows_per_partial, head_dim):
+    out = ctypes.c_size_t()
+    _check(_lib.pkv_workspace_bytes(num_partials, rows_per_partial, head_dim, ctypes.byref(out)),
+           "pkv_workspace_bytes")
+    return out.value
+
+
+def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, worker_offsets,
+                       req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
+                       batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
+                       kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
+                       stream=None):
+    """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.block_table, a.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    a.items, a.worker_offsets, a.req_tile_base = _ptr(items), _ptr(worker_offsets), _ptr(req_tile_base)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    a.num_items, a.num_partials, a.num_pages = num_items, num_partials, num_pages
+    a.batch, a.q_len, a.num_q_heads, a.num_kv_heads = batch, q_len, num_q_heads, num_kv_heads
+    a.head_dim, a.page_size, a.bt_stride = head_dim, page_size, bt_stride
+    a.kv_format = KV_FORMATS.get(kv_format, kv_format)
+    a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
+    _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
+
+
+def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batch, q_len,
+                num_q_heads, num_kv_heads, head_dim, out, lse_out=None, stream=None):
+    """Enqueue the log-sum-exp combine kernel."""
+    _check(_lib.pkv_combine(_ptr(workspace), workspace_bytes, num_partials, _ptr(req_tile_base),
+                            batch, q_len, num_q_heads, num_kv_heads, head_dim, _ptr(out),
+                            _ptr(lse_out), _stream_handle(stream)), "pkv_combine")
+
+
+# ---------------------------------------------------------------------------------
+# Per-step runner
+
+
+class PagedDecode:
+    """One decode step = host plan + one H2D copy of the plan + decode_partial + combine,
+    all enqueued on the current torch stream with no host synchronisation.
+
+    Pinned plan buffers are used round-robin and each is reused only after the copy
+    that read it has completed. Device buffers (plan, workspace) grow on demand and
+    are kept, so after the first step no allocation happens at a fixed shape."""
+
+    def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
+                 q_len=1, tile_tokens=0, num_workers=0, device=None, pinned_slots=3):
+        import torch
+        self.torch = torch
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.head_dim, self.page_size, self.kv_format = head_dim, page_size, kv_format
+        self.q_len, self.tile_tokens = q_len, tile_tokens
+        self.rows = (num_q_heads // num_kv_heads) * q_len
+        self.num_workers = num_workers or pkv_default_num_workers(self.device.index, kv_format, head_dim)
+        self._pinned = [None] * pinned_slots
+        self._events = [None] * pinned_slots
+        self._slot = 0
+        self._dev_plan = None
+        self._workspace = None
+        self.last_plan = None
+
+    def plan(self, seq_lens_h):
+        """Host plan into a pinned buffer; returns a dict describing it."""
+        torch = self.torch
+        sl = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
+        T, N, NP = pkv_plan_query(sl, self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                                  self.page_size, self.kv_format, self.tile_tokens, self.num_workers)
+        W, B = self.num_workers, len(sl)
+        n_off = 4 * N
+        n_rtb = n_off + _round4(W + 1)
+        n_sl = n_rtb + _round4(B + 1)
+        total = n_sl + _round4(B)
+        k = self._slot
+        self._slot = (k + 1) % len(self._pinned)
+        if self._events[k] is not None:
+            self._events[k].synchronize()          # the copy that last read this buffer is done
+        buf = self._pinned[k]
+        if buf is None or buf.numel() < total:
+            buf = torch.empty(max(total, 1024), dtype=torch.int32, pin_memory=True)
+            self._pinned[k] = buf
+        h = buf.numpy()
+        pkv_plan(sl, self.q_len, self.num_kv_heads, T, W,
+                 out=(h[:n_off].reshape(N, 4), h[n_off:n_off + W + 1], h[n_rtb:n_rtb + B + 1]))
+        h[n_sl:n_sl + B] = sl
+        p = dict(T=T, N=N, NP=NP, W=W, B=B, total=total, n_off=n_off, n_rtb=n_rtb, n_sl=n_sl, slot=k)
+        self.last_plan = p
+        return p
+
+    def upload(self, p):
+        torch = self.torch
+        if self._dev_plan is None or self._dev_plan.numel() < p["total"]:
+            self._dev_plan = torch.empty(max(p["total"], 1024), dtype=torch.int32, device=self.device)
+        self._dev_plan[:p["total"]].copy_(self._pinned[p["slot"]][:p["total"]], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._events[p["slot"]] = ev
+        d = self._dev_plan
+        return (d[:p["n_off"]], d[p["n_off"]:p["n_rtb"]], d[p["n_rtb"]:p["n_sl"]],
+                d[p["n_sl"]:p["n_sl"] + p["B"]])
+
+    def workspace(self, num_partials):
+        nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)
+        if self._workspace is None or self._workspace.numel() < nbytes:
+            self._workspace = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
+        return self._workspace, nbytes
+
+    def __call__(self, q, k_cache, v_cache, block_table, seq_lens_h, scale, *, k_scale=None,
+                 v_scale=None, seq_lens=None, out=None, lse_out=None, stream=None):
+        """Run one decode step. ``seq_lens_h`` (host ints) drives the plan; ``seq_lens``
+        (device int32) defaults to a copy uploaded with the plan."""
+        torch = self.torch
+        p = self.plan(seq_lens_h)
+        items, offs, rtb, sl_dev = self.upload(p)
+        if seq_lens is None:
+            seq_lens = sl_dev
+        ws, ws_bytes = self.workspace(p["NP"])
+        B = p["B"]
+        if out is None:
+            out = torch.empty((B, self.q_len, self.num_q_heads, self.head_dim), dtype=torch.bfloat16,
+                              device=self.device)
+        pkv_decode_partial(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                           seq_lens=seq_lens, items=items, worker_offsets=offs, req_tile_base=rtb,
+                           workspace=ws, workspace_bytes=ws_bytes, num_items=p["N"],
+                           num_partials=p["NP"], num_pages=k_cache.shape[0], batch=B,
+                           q_len=self.q_len, num_q_heads=self.num_q_heads,
+                           num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
+                           page_size=self.page_size, bt_stride=block_table.shape[1],
+                           kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
+                           scale=scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
+        pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"], req_tile_base=rtb,
+                    batch=B, q_len=self.q_len, num_q_heads=self.num_q_heads,
+                    num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, out=out, lse_out=lse_out,
+                    stream=stream)
+        return out
+
+
+def _round4(x):
+    return (x + 3) // 4 * 4

@@ -1,0 +1,278 @@
+// C ABI of libpkv.so (declared in include/pkv.h): argument validation, status
+// reporting, the host planner entry points and the kernel launches.
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+#include "planner.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr float kLog2e = 1.44269504088896341f;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Shape rules shared by every entry point.
+int check_shape(int q_len, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                int kv_format) {
+  if (kv_format != PKV_KV_BF16 && kv_format != PKV_KV_FP8_E4M3FN)
+    return fail(PKV_ERR_INVALID_ARG, "kv_format %d is not a pkv_kv_format", kv_format);
+  if (num_q_heads < 1 || num_kv_heads < 1 || q_len < 1 || head_dim < 1 || page_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive (q_len %d, heads %d/%d, D %d, P %d)",
+                q_len, num_q_heads, num_kv_heads, head_dim, page_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (page_size % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
+  if (kv_format == PKV_KV_FP8_E4M3FN && page_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "fp8 KV needs page_size 64 (one scale per 64-token tile), got %d",
+                page_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (q_len > 4) return fail(PKV_ERR_UNSUPPORTED, "q_len %d (supported: 1..4)", q_len);
+  const int rows = (num_q_heads / num_kv_heads) * q_len;
+  if (rows > pkv::kMaxRows)
+    return fail(PKV_ERR_UNSUPPORTED, "group size x q_len = %d rows per kv head (max %d)", rows,
+                pkv::kMaxRows);
+  return PKV_OK;
+}
+
+int check_seq_lens(int batch, const int32_t* seq_lens_h, int q_len) {
+  for (int b = 0; b < batch; ++b) {
+    const int32_t L = seq_lens_h[b];
+    if (L < 1 || L < q_len)
+      return fail(PKV_ERR_SEQ, "seq_lens[%d] = %d (needs >= max(1, q_len = %d))", b, L, q_len);
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case PKV_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_SEQ: return "sequence length shorter than the query tokens or zero";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_plan_query(int batch, const int32_t* seq_lens_h, int q_len, int num_q_heads,
+                   int num_kv_heads, int head_dim, int page_size, int kv_format, int tile_tokens,
+                   int num_workers, int32_t* tile_tokens_out, int64_t* num_items_out,
+                   int64_t* num_partials_out) {
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if ((batch > 0 && seq_lens_h == nullptr) || tile_tokens_out == nullptr ||
+      num_items_out == nullptr || num_partials_out == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_workers < 1) return fail(PKV_ERR_INVALID_ARG, "num_workers %d < 1", num_workers);
+  if (tile_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "tile_tokens %d < 0", tile_tokens);
+  int st = check_shape(q_len, num_q_heads, num_kv_heads, head_dim, page_size, kv_format);
+  if (st != PKV_OK) return st;
+  st = check_seq_lens(batch, seq_lens_h, q_len);
+  if (st != PKV_OK) return st;
+  const bool fp8 = kv_format == PKV_KV_FP8_E4M3FN;
+  const int64_t quantum = pkv::tile_quantum(page_size, fp8);
+  int64_t T = tile_tokens;
+  if (T == 0) {
+    T = pkv::auto_tile_tokens(batch, seq_lens_h, q_len, num_q_heads, num_kv_heads, head_dim,
+                              page_size, fp8, num_workers);
+  } else if (T % quantum != 0) {
+    return fail(PKV_ERR_UNSUPPORTED, "tile_tokens %d is not a multiple of the quantum %lld",
+                tile_tokens, static_cast<long long>(quantum));
+  }
+  const pkv::PlanStats s = pkv::plan_stats(batch, seq_lens_h, num_kv_heads, T, num_workers);
+  if (s.num_items > INT32_MAX / 4)
+    return fail(PKV_ERR_UNSUPPORTED, "plan of %lld items is too large",
+                static_cast<long long>(s.num_items));
+  *tile_tokens_out = static_cast<int32_t>(T);
+  *num_items_out = s.num_items;
+  *num_partials_out = s.num_items;
+  return PKV_OK;
+}
+
+int pkv_plan(int batch, const int32_t* seq_lens_h, int q_len, int num_kv_heads, int tile_tokens,
+             int num_workers, int32_t* items_h, int32_t* worker_offsets_h,
+             int32_t* req_tile_base_h) {
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if ((batch > 0 && (seq_lens_h == nullptr || items_h == nullptr)) ||
+      worker_offsets_h == nullptr || req_tile_base_h == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_workers < 1) return fail(PKV_ERR_INVALID_ARG, "num_workers %d < 1", num_workers);
+  if (tile_tokens < 1) return fail(PKV_ERR_INVALID_ARG, "tile_tokens %d < 1", tile_tokens);
+  if (num_kv_heads < 1 || q_len < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads %d and q_len %d must be positive", num_kv_heads,
+                q_len);
+  const int st = check_seq_lens(batch, seq_lens_h, q_len);
+  if (st != PKV_OK) return st;
+  pkv::build_plan(batch, seq_lens_h, num_kv_heads, tile_tokens, num_workers, items_h,
+                  worker_offsets_h, req_tile_base_h);
+  return PKV_OK;
+}
+
+int pkv_default_num_workers(int device, int kv_format, int head_dim, int* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (kv_format != PKV_KV_BF16 && kv_format != PKV_KV_FP8_E4M3FN)
+    return fail(PKV_ERR_INVALID_ARG, "kv_format %d is not a pkv_kv_format", kv_format);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  int cus = 0;
+  const hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "hipDeviceGetAttribute(device %d): %s", device, hipGetErrorString(e));
+  *out = cus * pkv::kDecodeGroupsPerCU;
+  return PKV_OK;
+}
+
+int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim, size_t* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_partials < 0 || rows_per_partial < 1 || head_dim < 1)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes (partials %lld, rows %d, D %d)",
+                static_cast<long long>(num_partials), rows_per_partial, head_dim);
+  const size_t o = static_cast<size_t>(num_partials) * rows_per_partial * head_dim * 4;
+  const size_t l = static_cast<size_t>(num_partials) * rows_per_partial * 4;
+  *out = align256(o) + align256(l);
+  return PKV_OK;
+}
+
+int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
+  if (a == nullptr) return fail(PKV_ERR_INVALID_ARG, "null args");
+  if (a->struct_size < sizeof(pkv_decode_args))
+    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size,
+                sizeof(pkv_decode_args));
+  int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
+                       a->kv_format);
+  if (st != PKV_OK) return st;
+  if (a->batch < 0 || a->num_items < 0 || a->num_partials < a->num_items || a->num_pages < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size or num_partials < num_items");
+  if (a->num_workers < 1) return fail(PKV_ERR_INVALID_ARG, "num_workers %d < 1", a->num_workers);
+  const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
+  const int64_t quantum = pkv::tile_quantum(a->page_size, fp8);
+  if (a->tile_tokens < 1 || a->tile_tokens % quantum != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "tile_tokens %d is not a positive multiple of %lld",
+                a->tile_tokens, static_cast<long long>(quantum));
+  if (a->num_items == 0) return PKV_OK;
+  if (a->batch < 1 || a->num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, "work items given for an empty batch or cache");
+  const int max_pages = static_cast<int>(pkv::ceil_div(INT32_MAX, a->page_size));
+  if (a->bt_stride < 1 || a->bt_stride > max_pages)
+    return fail(PKV_ERR_INVALID_ARG, "bt_stride %d out of range", a->bt_stride);
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens || !a->items ||
+      !a->worker_offsets || !a->req_tile_base || !a->workspace)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (fp8 != (a->k_scale != nullptr) || fp8 != (a->v_scale != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale must be given exactly for fp8 KV");
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
+      !aligned(a->workspace, 16))
+    return fail(PKV_ERR_ALIGNMENT, "q, k_cache, v_cache and workspace must be 16-byte aligned");
+  if (!aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) || !aligned(a->items, 16) ||
+      !aligned(a->worker_offsets, 4) || (fp8 && (!aligned(a->k_scale, 4) || !aligned(a->v_scale, 4))))
+    return fail(PKV_ERR_ALIGNMENT, "int32/fp32 arrays misaligned (items need 16 bytes)");
+  const int rows = (a->num_q_heads / a->num_kv_heads) * a->q_len;
+  size_t need = 0;
+  pkv_workspace_bytes(a->num_partials, rows, a->head_dim, &need);
+  if (a->workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes, need);
+  if (!std::isfinite(a->scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+
+  pkv::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k_cache = static_cast<const uint8_t*>(a->k_cache);
+  p.v_cache = static_cast<const uint8_t*>(a->v_cache);
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.items = a->items;
+  p.worker_offsets = a->worker_offsets;
+  p.ws_o = static_cast<float*>(a->workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) +
+                                      align256(static_cast<size_t>(a->num_partials) * rows *
+                                               a->head_dim * 4));
+  p.q_len = a->q_len;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.rows = rows;
+  p.page_size = a->page_size;
+  p.bt_stride = a->bt_stride;
+  p.tile_tokens = a->tile_tokens;
+  p.qk_scale_log2 = a->scale * kLog2e;
+  const hipError_t e = pkv::launch_decode_partial(p, a->head_dim, fp8, a->num_workers,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_partial launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_partials,
+                const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
+                int num_kv_heads, int head_dim, void* out, float* lse_out, void* stream) {
+  const int st = check_shape(q_len, num_q_heads, num_kv_heads, head_dim, 16, PKV_KV_BF16);
+  if (st != PKV_OK) return st;
+  if (batch < 0 || num_partials < 0)
+    return fail(PKV_ERR_INVALID_ARG, "batch %d / num_partials %lld negative", batch,
+                static_cast<long long>(num_partials));
+  if (batch == 0) return PKV_OK;
+  if (static_cast<int64_t>(batch) * q_len * num_q_heads > INT32_MAX / 64)
+    return fail(PKV_ERR_UNSUPPORTED, "too many output rows");
+  if (!workspace || !req_tile_base || !out) return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(workspace, 16) || !aligned(out, 16) || !aligned(req_tile_base, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return fail(PKV_ERR_ALIGNMENT, "workspace and out must be 16-byte aligned");
+  const int rows = (num_q_heads / num_kv_heads) * q_len;
+  size_t need = 0;
+  pkv_workspace_bytes(num_partials, rows, head_dim, &need);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  pkv::CombineParams p;
+  p.ws_o = static_cast<const float*>(workspace);
+  p.ws_lse = reinterpret_cast<const float*>(
+      static_cast<const char*>(workspace) +
+      align256(static_cast<size_t>(num_partials) * rows * head_dim * 4));
+  p.req_tile_base = req_tile_base;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse_out = lse_out;
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.rows = rows;
+  const hipError_t e = pkv::launch_combine(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // extern "C"

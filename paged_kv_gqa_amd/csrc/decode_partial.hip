@@ -1,0 +1,449 @@
+// Split-KV partial attention for paged-KV GQA decode on gfx950.
+//
+// One persistent workgroup per planner worker walks its work items (b, g, i): the
+// uniform KV tiles that the per-step greedy bin-packing assigned to it (HPC-Ops
+// review, "How the kernels are organized around specific workload shapes"). For
+// each tile it writes a softmax-normalised partial output and its log-sum-exp, to
+// be merged by the combine kernel.
+//
+// Mapping onto CDNA4 (wave64, MFMA 16x16x32 bf16):
+// - The four waves of a workgroup split a tile into 32-token chunks, round-robin.
+//   A chunk is two 16-token halves; each half lies inside one page because pages
+//   and tiles are multiples of 16 tokens.
+// - Operands are swapped so the KV tokens fill the MFMA's 16-row side and the
+//   M = G*Tq query rows of the kv head sit on the 16-column side (the "swap A/B"
+//   idea of the HPC-Ops launch article, section on aligning task traits with the
+//   hardware, re-derived for MFMA). Lane l owns query row n = l % 16 for the whole
+//   softmax, so row max, row sum and rescale factors never leave the lane except
+//   for one exchange across the four 16-lane groups.
+// - K and V are read straight from HBM with 16-byte loads in their natural
+//   [page][head][token][d] layout: lane l reads token (l % 16) of a half, bytes
+//   16*(l/16) + 64*u of its row, exactly the MFMA A-operand layout. QK^T needs no
+//   shuffling. P.V contracts over tokens, so V is transposed on the matrix core: an
+//   MFMA of the V half against a 0/1 selection matrix returns, in each lane, four
+//   consecutive tokens of one head dimension - the operand layout P.V needs -
+//   exactly (products by 1 and sums of zeros), in fp32, then packed back to bf16.
+// - FP8 (OCP e4m3fn) K/V bytes are widened to bf16 with the gfx950 conversion
+//   instruction (exact). The per-(page, kv head) scales are applied outside the
+//   products: the K scale multiplies the scores, the V scale multiplies P before P.V.
+// - The next chunk's loads are issued before the current chunk is computed, so each
+//   wave keeps 16 KB (bf16) of KV in flight while its matrix and vector work runs.
+#include "kernels.hpp"
+
+#include <math.h>
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = kDecodeWaves;
+constexpr int kThreads = kWaves * 64;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Eight e4m3fn bytes (two dwords) -> eight bf16 (four dwords), exact.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(unsigned w0, unsigned w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return r;
+}
+
+// Max over the four 16-lane groups (lanes n, n+16, n+32, n+48) with the gfx950
+// lane-swap instructions: each swap returns the value and its partner in every lane.
+__device__ __forceinline__ float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int D, bool FP8>
+struct Cfg {
+  static constexpr int kEb = FP8 ? 1 : 2;        // bytes per KV element
+  static constexpr int kSteps = D / 32;           // MFMA k-steps over the head dimension
+  static constexpr int kLoads = D * kEb / 64;     // 16-byte loads per lane per half
+  static constexpr int kBlocks = D / 16;          // 16-wide head-dim blocks of the output
+  static constexpr int kRowBytes = D * kEb;
+};
+
+// Head-dimension index that k-step s, lane group gq, element e of an MFMA operand
+// holds. bf16: one 16-byte load per step. fp8: one 16-byte load serves two steps.
+template <bool FP8>
+__device__ __forceinline__ int op_dim(int s, int gq, int e) {
+  if (FP8) return 64 * (s >> 1) + 16 * gq + 8 * (s & 1) + e;
+  return 32 * s + 8 * gq + e;
+}
+
+// Head-dimension index of output value v in block (s, c) of lane group gq: the
+// selection matrix c picks operand column k = 16c + r, r = 4*gq + v.
+template <bool FP8>
+__device__ __forceinline__ int out_dim(int s, int c, int gq, int v) {
+  const int k = 16 * c + 4 * gq + v;
+  return op_dim<FP8>(s, k >> 3, k & 7);
+}
+
+template <int D, bool FP8>
+struct Chunk {
+  u32x4 k[2][Cfg<D, FP8>::kLoads];
+  u32x4 v[2][Cfg<D, FP8>::kLoads];
+};
+
+struct ItemCtx {
+  const int32_t* __restrict__ bt;  // block-table row of the request
+  int64_t head_off;                // byte offset of kv head g inside a page
+  int64_t page_bytes;              // bytes of one page (all heads)
+  int tile_start, tile_end, page_size, row_bytes;
+};
+
+// Byte offsets of the two 16-token halves of a chunk (wave-uniform; the block-table
+// reads are scalar loads). A half past the tile end re-reads half 0 (masked later).
+struct HalfOffsets {
+  int64_t off[2];
+};
+
+__device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chunk) {
+  HalfOffsets r;
+  const int j0 = it.tile_start + 32 * chunk;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int jh = j0 + 16 * h;
+    if (jh >= it.tile_end) jh = j0;
+    const int page = jh / it.page_size;
+    const int64_t phys = it.bt[page];
+    r.off[h] = phys * it.page_bytes + it.head_off +
+               static_cast<int64_t>(jh - page * it.page_size) * it.row_bytes;
+  }
+  return r;
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_chunk(Chunk<D, FP8>& ch, const uint8_t* __restrict__ kc,
+                                           const uint8_t* __restrict__ vc, const HalfOffsets& ho,
+                                           int lane_off) {
+  using C = Cfg<D, FP8>;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t off = ho.off[h] + lane_off;
+#pragma unroll
+    for (int u = 0; u < C::kLoads; ++u) {
+      ch.k[h][u] = *reinterpret_cast<const u32x4*>(kc + off + 64 * u);
+      ch.v[h][u] = *reinterpret_cast<const u32x4*>(vc + off + 64 * u);
+    }
+  }
+}
+
+// Online-softmax update of one 32-token chunk. acc[blk] holds O^T for head-dim
+// block blk (lane: rows 4*gq+v of the block, column n); m in log2 units.
+template <int D, bool FP8>
+__device__ __forceinline__ void process_chunk(const Chunk<D, FP8>& ch, const u32x4 (&qf)[D / 32],
+                                              const u32x4 (&sel)[2], f32x4 (&acc)[D / 16],
+                                              float& m, float& lsum, int j0, int lim,
+                                              int tile_end, float c_qk, float v_mul, int n,
+                                              int gq) {
+  using C = Cfg<D, FP8>;
+  u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      if constexpr (FP8) {
+        const u32x4 kr = ch.k[h][s >> 1], vr = ch.v[h][s >> 1];
+        kop[h][s] = (s & 1) ? fp8x8_to_bf16(kr[2], kr[3]) : fp8x8_to_bf16(kr[0], kr[1]);
+        vop[h][s] = (s & 1) ? fp8x8_to_bf16(vr[2], vr[3]) : fp8x8_to_bf16(vr[0], vr[1]);
+      } else {
+        kop[h][s] = ch.k[h][s];
+        vop[h][s] = ch.v[h][s];
+      }
+    }
+  }
+  // Tokens at or past the tile end may be unwritten cache memory: zero their V so
+  // that a zero probability cannot meet a NaN in P.V. Lane l loaded token l % 16.
+  if (j0 + 32 > tile_end) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (j0 + 16 * h + n >= tile_end) {
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) vop[h][s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // S^T = K . Q^T: lane (n, gq) gets tokens 16h + 4gq + v of query row n.
+  f32x4 st[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    st[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) st[h] = mfma_bf16(kop[h][s], qf[s], st[h]);
+  }
+  float sv[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + 16 * h + 4 * gq + v;
+      sv[4 * h + v] = (j < lim) ? st[h][v] * c_qk : -INFINITY;
+    }
+  }
+  float cm = sv[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+  cm = group_max(cm);
+  const float m_new = fmaxf(m, cm);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+  unsigned pk[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
+    const float p1 = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
+    const unsigned u = pack_bf16(p0, p1);
+    psum += bf16_lo(u) + bf16_hi(u);   // the row sum uses the rounded weights of P.V
+    pk[e] = FP8 ? pack_bf16(p0 * v_mul, p1 * v_mul) : u;
+  }
+  lsum = lsum * alpha + psum;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
+  }
+  m = m_new;
+  const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
+
+  // V^T via the selection MFMA, then O^T += V^T . P^T.
+#pragma unroll
+  for (int s = 0; s < C::kSteps; ++s) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 x0 = mfma_bf16(vop[0][s], sel[c], zero);
+      const f32x4 x1 = mfma_bf16(vop[1][s], sel[c], zero);
+      const u32x4 va = {pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]),
+                        pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
+      acc[2 * s + c] = mfma_bf16(va, pb, acc[2 * s + c]);
+    }
+  }
+}
+
+// Scalar shape arguments of the decode kernel.
+struct DecodeShape {
+  int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
+  float qk_scale_log2;
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_cache,
+    const uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
+    const int32_t* __restrict__ worker_offsets, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse, const DecodeShape sh) {
+  using C = Cfg<D, FP8>;
+  constexpr int kLdsStride = D + 4;
+  __shared__ float lds_o[kWaves][kMaxRows][kLdsStride];
+  __shared__ float lds_m[kWaves][kMaxRows];
+  __shared__ float lds_l[kWaves][kMaxRows];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int n = lane & 15;   // query row owned by this lane (and K/V row it loads)
+  const int gq = lane >> 4;  // 16-lane group
+
+  // Selection matrices: sel[c] has a 1 where operand k = 16c + n (bf16 1.0 = 0x3f80).
+  u32x4 sel[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int e = 16 * c + n - 8 * gq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      sel[c][w] = (e == 2 * w ? 0x3f80u : 0u) | (e == 2 * w + 1 ? 0x3f800000u : 0u);
+  }
+
+  const int M = sh.rows;
+  const int Tq = sh.q_len;
+  const int G = sh.group;
+  const int lane_off = n * C::kRowBytes + 16 * gq;
+  const int first = worker_offsets[blockIdx.x];
+  const int last = worker_offsets[blockIdx.x + 1];
+
+  for (int itx = first; itx < last; ++itx) {
+    const int b = items[4 * itx + 0];
+    const int g = items[4 * itx + 1];
+    const int ti = items[4 * itx + 2];
+    const int slot = items[4 * itx + 3];
+    const int L = seq_lens[b];
+
+    ItemCtx it;
+    it.bt = block_table + static_cast<int64_t>(b) * sh.bt_stride;
+    it.row_bytes = C::kRowBytes;
+    it.head_off = static_cast<int64_t>(g) * sh.page_size * C::kRowBytes;
+    it.page_bytes = static_cast<int64_t>(sh.num_kv_heads) * sh.page_size * C::kRowBytes;
+    it.tile_start = ti * sh.tile_tokens;
+    it.tile_end = min(L, it.tile_start + sh.tile_tokens);
+    it.page_size = sh.page_size;
+
+    // Query fragment of row n (zero for padding rows n >= M) and its causal limit.
+    u32x4 qf[C::kSteps];
+    int lim = it.tile_end;
+    if (n < M) {
+      const int t = n / G;
+      const int head = g * G + (n - t * G);
+      const uint16_t* qrow = q + ((static_cast<int64_t>(b) * Tq + t) * sh.num_q_heads + head) * D;
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s)
+        qf[s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
+      lim = min(lim, L - Tq + t + 1);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 acc[C::kBlocks];
+#pragma unroll
+    for (int bl = 0; bl < C::kBlocks; ++bl) acc[bl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int nchunks = (it.tile_end - it.tile_start + 31) >> 5;
+    float c_qk = sh.qk_scale_log2, v_mul = 1.f;
+    auto chunk_scales = [&](int chunk) {
+      if constexpr (FP8) {
+        const int j0 = it.tile_start + 32 * chunk;
+        const int64_t sidx = static_cast<int64_t>(it.bt[j0 / it.page_size]) * sh.num_kv_heads + g;
+        c_qk = sh.qk_scale_log2 * k_scale[sidx];
+        v_mul = v_scale[sidx];
+      }
+    };
+
+    // Two register buffers alternate: while one chunk is computed the next one's
+    // loads are in flight, and the block-table offsets of the one after are read.
+    // Past the wave's last chunk the prefetch repeats the wave's own latest chunk
+    // (a cache hit), so every iteration issues the same loads.
+    int c0 = wid;
+    if (c0 < nchunks) {
+      Chunk<D, FP8> A, B;
+      HalfOffsets hoA = chunk_offsets(it, c0);
+      load_chunk<D, FP8>(A, k_cache, v_cache, hoA, lane_off);
+      int c1 = c0 + kWaves;
+      HalfOffsets hoB = c1 < nchunks ? chunk_offsets(it, c1) : hoA;
+      for (;;) {
+        load_chunk<D, FP8>(B, k_cache, v_cache, hoB, lane_off);
+        const int c2 = c1 + kWaves;
+        hoA = c2 < nchunks ? chunk_offsets(it, c2) : hoB;
+        chunk_scales(c0);
+        process_chunk<D, FP8>(A, qf, sel, acc, m, lsum, it.tile_start + 32 * c0, lim, it.tile_end,
+                              c_qk, v_mul, n, gq);
+        if (c1 >= nchunks) break;
+        load_chunk<D, FP8>(A, k_cache, v_cache, hoA, lane_off);
+        const int c3 = c2 + kWaves;
+        hoB = c3 < nchunks ? chunk_offsets(it, c3) : hoA;
+        chunk_scales(c1);
+        process_chunk<D, FP8>(B, qf, sel, acc, m, lsum, it.tile_start + 32 * c1, lim, it.tile_end,
+                              c_qk, v_mul, n, gq);
+        if (c2 >= nchunks) break;
+        c0 = c2;
+        c1 = c3;
+      }
+    }
+
+    // Wave result -> LDS: row max, full row sum, unnormalised O.
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (gq == 0) {
+      lds_m[wid][n] = m;
+      lds_l[wid][n] = lsum;
+    }
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lds_o[wid][n][out_dim<FP8>(s, c, gq, v)] = acc[2 * s + c][v];
+    __syncthreads();
+
+    // Merge the waves' partial softmax states and write the item's partial.
+    float* wo = ws_o + static_cast<int64_t>(slot) * M * D;
+    for (int e = tid; e < M * D; e += kThreads) {
+      const int r = e / D, d = e - r * D;
+      float mx = lds_m[0][r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w][r]);
+      float o = 0.f;
+      if (mx != -INFINITY) {
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = __builtin_amdgcn_exp2f(lds_m[w][r] - mx);
+          num += f * lds_o[w][r][d];
+          den += f * lds_l[w][r];
+        }
+        o = num / den;
+      }
+      wo[e] = o;
+    }
+    if (tid < M) {
+      float mx = lds_m[0][tid];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w][tid]);
+      float lse = -INFINITY;
+      if (mx != -INFINITY) {
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][tid] - mx) * lds_l[w][tid];
+        lse = (mx + __builtin_amdgcn_logf(den)) * kLn2;
+      }
+      ws_lse[static_cast<int64_t>(slot) * M + tid] = lse;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8, int num_workers,
+                                 hipStream_t stream) {
+  const dim3 grid(num_workers), block(kThreads);
+  const DecodeShape sh = {p.q_len, p.num_q_heads, p.num_kv_heads, p.group, p.rows,
+                          p.page_size, p.bt_stride, p.tile_tokens, p.qk_scale_log2};
+#define PKV_LAUNCH(DIM, F8)                                                                   \
+  hipLaunchKernelGGL((decode_partial_kernel<DIM, F8>), grid, block, 0, stream, p.q, p.k_cache, \
+                     p.v_cache, p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items,     \
+                     p.worker_offsets, p.ws_o, p.ws_lse, sh)
+  if (head_dim == 128) {
+    if (fp8)
+      PKV_LAUNCH(128, true);
+    else
+      PKV_LAUNCH(128, false);
+  } else {
+    if (fp8)
+      PKV_LAUNCH(64, true);
+    else
+      PKV_LAUNCH(64, false);
+  }
+#undef PKV_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace pkv

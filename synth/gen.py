@@ -83,17 +83,25 @@ _GRID = _e4m3fn_grid()
 
 
 def f32_to_e4m3fn(x):
-    """Encode float values to OCP e4m3fn codes: nearest magnitude, ties to the even
-    code, saturating to +-448. NaN inputs are not expected (inputs are finite)."""
-    x = np.asarray(x, dtype=np.float64)
-    mag = np.minimum(np.abs(x), E4M3_MAX)
-    hi = np.searchsorted(_GRID, mag, side="left")          # first grid value >= mag
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = mag - _GRID[lo]
-    d_hi = _GRID[hi] - mag
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(mag == _GRID[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    """Encode float values to OCP e4m3fn codes: nearest representable magnitude, ties
+    to the even code, saturating to +-448. Inputs are finite; they are taken as
+    float32, in which every step below is exact.
+
+    Within a binade [2^e, 2^(e+1)) (e >= -6) the spacing is 2^(e-3); below 2^-6 it is
+    2^-9. Rounding mag / spacing to the nearest integer (ties to even) and reading the
+    code back from the rounded value gives the code; a rounding up to 2^(e+1) lands on
+    the next binade's first code."""
+    x = np.asarray(x, dtype=np.float32)
+    mag = np.minimum(np.abs(x), np.float32(E4M3_MAX))
+    _, ex = np.frexp(mag)                         # mag = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                    # binade exponent (subnormals share -6)
+    step = np.ldexp(np.float32(1.0), e - 3).astype(np.float32)
+    q = np.rint(mag / step) * step               # round half to even
+    _, qx = np.frexp(q)
+    qe = qx - 1
+    normal = q >= np.float32(2.0 ** -6)
+    m = np.where(normal, np.ldexp(q, -np.maximum(qe, -6)) * 8 - 8, q * 512)
+    code = np.where(normal, ((qe + 7) << 3) + m, m).astype(np.uint8)
     sign = (np.signbit(x) & (code != 0)).astype(np.uint8) << 7
     return code | sign
 

@@ -1,0 +1,198 @@
+"""The C-ABI library on the host (no GPU calls): symbols, version, the native planner
+bit for bit against the reference planner, and the argument checks that return
+before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import paged_kv_gqa_amd as pkv
+import synth
+from oracle import plan as ref_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = f.read()
+    # declarations: a return type at the start of a line, then the function name
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(pkv_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) == 9
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(pkv, n), n          # and the binding mirrors it
+
+
+def test_version_and_status_strings():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        ver = int(re.search(r"#define PKV_ABI_VERSION (\d+)", f.read()).group(1))
+    assert pkv.pkv_abi_version() == ver
+    for code in range(0, -7, -1):
+        assert pkv.pkv_status_string(code) not in ("", "unknown status")
+    assert pkv.pkv_status_string(-99) == "unknown status"
+
+
+def native_plan(sl, q_len, Hq, Hkv, D, P, fmt, T, W):
+    T, N, NP = pkv.pkv_plan_query(sl, q_len, Hq, Hkv, D, P, fmt, T, W)
+    assert NP == N
+    items, offs, rtb = pkv.pkv_plan(sl, q_len, Hkv, T, W, num_items=N)
+    return T, items, offs, rtb
+
+
+def assert_same_plan(sl, q_len, Hq, Hkv, D, P, fmt, T, W):
+    Tn, items, offs, rtb = native_plan(sl, q_len, Hq, Hkv, D, P, fmt, T, W)
+    ref = ref_plan.plan(sl, q_len, Hq, Hkv, D, P, fmt, T, W)
+    assert Tn == ref["tile_tokens"]
+    assert np.array_equal(items, ref["items"])
+    assert np.array_equal(offs, ref["worker_offsets"])
+    assert np.array_equal(rtb, ref["req_tile_base"])
+
+
+@pytest.mark.parametrize("name", list(synth.ALL))
+@pytest.mark.parametrize("W", [256, 512, 1024])
+def test_plan_matches_reference_on_workloads(name, W):
+    cfg = synth.ALL[name]
+    sl = synth.draw_seq_lens(cfg, np.random.default_rng(0))
+    args = (sl, cfg["q_len"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"],
+            cfg["page_size"], cfg["kv_format"])
+    assert_same_plan(*args, 0, W)
+    quantum = ref_plan.tile_quantum(cfg["page_size"], cfg["kv_format"])
+    assert_same_plan(*args, quantum * 8, W)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.integers(1, 5000), min_size=1, max_size=12), st.integers(1, 4),
+       st.sampled_from([16, 32, 64]), st.integers(1, 40), st.integers(0, 6), st.sampled_from(["bf16", "fp8"]),
+       st.integers(1, 4))
+def test_plan_matches_reference_fuzz(sl, Hkv, P, W, k, fmt, q_len):
+    if fmt == "fp8":
+        P = 64
+    sl = [max(L, q_len) for L in sl]
+    T = 0 if k == 0 else ref_plan.tile_quantum(P, fmt) * k
+    assert_same_plan(sl, q_len, Hkv * min(4, 16 // q_len), Hkv, 128, P, fmt, T, W)
+
+
+def test_plan_of_empty_batch():
+    T, N, NP = pkv.pkv_plan_query([], 1, 4, 1, 64, 16, "bf16", 0, 8)
+    assert N == 0 and NP == 0
+    items, offs, rtb = pkv.pkv_plan([], 1, 1, T, 8, num_items=0)
+    assert offs.tolist() == [0] * 9 and rtb.tolist() == [0]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(page_size=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8", page_size=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=4), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(q_len=5), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=4, q_len=4), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(num_workers=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(tile_tokens=-16), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kv_format=7), pkv.PKV_ERR_INVALID_ARG),
+    (dict(seq_lens=[5, 0]), pkv.PKV_ERR_SEQ),
+    (dict(seq_lens=[5, 2], q_len=3), pkv.PKV_ERR_SEQ),
+])
+def test_plan_query_errors(kw, status):
+    a = dict(seq_lens=[17, 64], q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16,
+             kv_format="bf16", tile_tokens=0, num_workers=4)
+    a.update(kw)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_query(a["seq_lens"], a["q_len"], a["num_q_heads"], a["num_kv_heads"], a["head_dim"],
+                           a["page_size"], a["kv_format"], a["tile_tokens"], a["num_workers"])
+    assert e.value.status == status
+    assert pkv.pkv_last_error() != ""
+
+
+def test_plan_errors():
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([3, 0], 1, 1, 16, 2, num_items=1)
+    assert e.value.status == pkv.PKV_ERR_SEQ
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([3], 1, 1, 0, 2, num_items=1)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([3], 1, 1, 16, 0, num_items=1)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_workspace_bytes():
+    o = 10 * 4 * 128 * 4
+    l = 10 * 4 * 4
+    assert pkv.pkv_workspace_bytes(10, 4, 128) == (o + 255) // 256 * 256 + (l + 255) // 256 * 256
+    assert pkv.pkv_workspace_bytes(0, 4, 128) == 0
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_workspace_bytes(-1, 4, 128)
+
+
+# Fake device addresses: every check below fails before the library makes a HIP call.
+A = 1 << 20
+
+
+def decode_kwargs(**kw):
+    base = dict(q=A, k_cache=2 * A, v_cache=3 * A, block_table=4 * A, seq_lens=5 * A, items=6 * A,
+                worker_offsets=7 * A, req_tile_base=8 * A, workspace=9 * A, workspace_bytes=1 << 30,
+                num_items=4, num_partials=4, num_pages=8, batch=2, q_len=1, num_q_heads=8,
+                num_kv_heads=2, head_dim=128, page_size=16, bt_stride=4, kv_format="bf16",
+                tile_tokens=32, num_workers=2, scale=0.1, stream=0)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=A + 8), pkv.PKV_ERR_ALIGNMENT),
+    (dict(workspace=9 * A + 4), pkv.PKV_ERR_ALIGNMENT),
+    (dict(items=6 * A + 4), pkv.PKV_ERR_ALIGNMENT),
+    (dict(workspace_bytes=100), pkv.PKV_ERR_WORKSPACE),
+    (dict(head_dim=80), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8", page_size=64, tile_tokens=64), pkv.PKV_ERR_INVALID_ARG),  # no scales
+    (dict(k_scale=10 * A), pkv.PKV_ERR_INVALID_ARG),                                  # bf16 with scales
+    (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_workers=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_partials=2), pkv.PKV_ERR_INVALID_ARG),
+    (dict(bt_stride=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_decode_partial_argument_errors(kw, status):
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode_partial(**decode_kwargs(**kw))
+    assert e.value.status == status
+
+
+def test_decode_partial_struct_size_checked():
+    a = pkv.DecodeArgs()
+    a.struct_size = 8
+    assert pkv._lib.pkv_decode_partial(ctypes.byref(a), None) == pkv.PKV_ERR_INVALID_ARG
+    assert pkv._lib.pkv_decode_partial(None, None) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_decode_partial_without_items_is_a_no_op():
+    pkv.pkv_decode_partial(**decode_kwargs(num_items=0, num_partials=0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=A + 2), pkv.PKV_ERR_ALIGNMENT),
+    (dict(workspace_bytes=16), pkv.PKV_ERR_WORKSPACE),
+    (dict(head_dim=32), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(out=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_partials=-1), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_combine_argument_errors(kw, status):
+    base = dict(workspace=9 * A, workspace_bytes=1 << 30, num_partials=4, req_tile_base=8 * A, batch=2,
+                q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128, out=A, stream=0)
+    base.update(kw)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_combine(**base)
+    assert e.value.status == status

@@ -1,0 +1,266 @@
+"""GPU parity of the HIP decode path against the fp64 oracle (needs an MI355X).
+
+Tolerances (the contract): max |gpu - oracle| <= 1e-2 on the bf16 output for BF16 KV
+and <= 3e-2 for FP8 KV, against the oracle on the same stored inputs. Tighter
+diagnostics are asserted too, because an absolute 1e-2 is loose at long L (outputs
+shrink like 1/sqrt(L)): relative L2 error <= 1e-2 and |lse - lse_ref| <= 1e-3. The
+arithmetic behind them: bf16 weights (relative 2^-9 each, averaging out), fp32
+accumulation, one bf16 rounding of the output (2^-9 relative).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.formats import E4M3FN_TABLE, bf16_bits_to_f64
+from tests.gpu_util import device_inputs, log, make_runner, max_abs, rel_l2, run_decode
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "fp8": 3e-2}
+REL_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_gqa_amd  # noqa: F401  (fails loudly without the built library)
+
+
+def cfg(**kw):
+    base = dict(name="case", batch=0, seq_lens=(1,), q_len=1, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, page_size=16, kv_format="bf16")
+    base.update(kw)
+    return base
+
+
+def check(inp, out, lse, pairs=None, tag=""):
+    ref_out, ref_lse = oracle.decode_attention(inp, pairs=pairs)
+    if pairs is not None:
+        sel = np.zeros(ref_lse.shape, dtype=bool)
+        G = inp.num_q_heads // inp.num_kv_heads
+        for b, g in pairs:
+            sel[b, :, g * G:(g + 1) * G] = True
+        out, ref_out = out[sel], ref_out[sel]
+        lse, ref_lse = lse[sel], ref_lse[sel]
+    assert np.isfinite(out).all() and np.isfinite(lse).all(), tag
+    ea, er, el = max_abs(out, ref_out), rel_l2(out, ref_out), max_abs(lse, ref_lse)
+    log("  %s: max_abs %.3e rel_l2 %.3e lse %.3e" % (tag, ea, er, el))
+    assert ea <= TOL[inp.kv_format], tag
+    assert er <= REL_TOL, tag
+    assert el <= LSE_TOL, tag
+
+
+SMALL = [
+    dict(id="tiny_auto", c=synth.TINY, T=0, W=0),
+    dict(id="tiny_T16_W1", c=synth.TINY, T=16, W=1),
+    dict(id="tiny_T64_W3", c=synth.TINY, T=64, W=3),
+    dict(id="g4_d128_p16", c=cfg(), sl=[1, 15, 16, 17, 33, 100, 257, 700], T=64, W=7),
+    dict(id="g4_d128_p16_T48", c=cfg(), sl=[31, 32, 47, 48, 49, 95, 96, 97], T=48, W=3),
+    dict(id="g8_d128_p64", c=cfg(num_q_heads=16, page_size=64), sl=[63, 64, 65, 500, 1000], T=128, W=5),
+    dict(id="g1_d64_p32", c=cfg(num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=32),
+         sl=[3, 90, 333], T=32, W=2),
+    dict(id="g16_d128", c=cfg(num_q_heads=16, num_kv_heads=1), sl=[40, 300, 2049], T=256, W=3),
+    dict(id="spec4_g4", c=cfg(q_len=4), sl=[4, 5, 6, 7, 33, 34, 35, 129], T=32, W=4),
+    dict(id="spec2_g8_d64", c=cfg(q_len=2, num_q_heads=16, head_dim=64), sl=[2, 17, 48, 49], T=16, W=3),
+    dict(id="spec3_g4_auto", c=cfg(q_len=3), sl=[3, 300, 1000, 4097], T=0, W=11),
+    dict(id="fp8_spec4", c=cfg(kv_format="fp8", page_size=64, q_len=4),
+         sl=[4, 64, 65, 66, 67, 200, 513], T=64, W=5),
+    dict(id="fp8_d64", c=cfg(kv_format="fp8", page_size=64, num_q_heads=4, num_kv_heads=1, head_dim=64),
+         sl=[1, 100, 1000], T=128, W=2),
+    dict(id="fp8_auto_g8", c=cfg(kv_format="fp8", page_size=64, num_q_heads=16, q_len=2),
+         sl=[2, 777, 3000, 64 * 65 + 1], T=0, W=9),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c["id"] for c in SMALL])
+def test_small_cases_match_oracle(case):
+    c = dict(case["c"])
+    inp = synth.make_inputs(c, seed=17, poison=True, slack_pages=3, seq_lens=case.get("sl"))
+    log("case %s B=%d Tq=%d G=%d D=%d P=%d %s T=%d W=%d" % (
+        case["id"], inp.batch, inp.q_len, inp.num_q_heads // inp.num_kv_heads, inp.head_dim,
+        inp.page_size, inp.kv_format, case["T"], case["W"]))
+    out, lse, _ = run_decode(inp, case["T"], case["W"])
+    check(inp, out, lse, tag=case["id"])
+
+
+def sample_pairs(inp, n=10, seed=0):
+    rng = np.random.default_rng(seed)
+    sl = inp.seq_lens
+    picks = {int(np.argmax(sl)), int(np.argmin(sl))}
+    picks |= set(int(b) for b in rng.choice(inp.batch, size=min(n, inp.batch), replace=False))
+    return sorted({(b, int(rng.integers(inp.num_kv_heads))) for b in picks} | {(int(np.argmax(sl)), 0)})
+
+
+@pytest.mark.parametrize("name", ["llama8b", "mixed", "long", "fp8_spec"])
+def test_full_size_workloads_sampled(name):
+    """The full workloads in the launch configuration the bench times (automatic tile
+    size, default worker count); the oracle checks sampled (request, kv head) groups."""
+    import torch
+    log("full-size %s: generating inputs" % name)
+    inp = synth.make_inputs(synth.ALL[name], seed=0)
+    log("full-size %s: running" % name)
+    out, lse, _ = run_decode(inp)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    check(inp, out, lse, pairs=sample_pairs(inp), tag=name)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def medium_inputs(fmt="bf16", seed=5, **kw):
+    c = cfg(num_q_heads=32, num_kv_heads=8, kv_format=fmt, page_size=64 if fmt == "fp8" else 16, **kw)
+    sl = [1, 64, 300, 1023, 2500, 4096]
+    return synth.make_inputs(c, seed=seed, slack_pages=5, seq_lens=[max(x, c["q_len"]) for x in sl])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_bitwise_repeatable(fmt):
+    inp = medium_inputs(fmt)
+    dev = device_inputs(inp)
+    _, l1, b1 = run_decode(inp, dev=dev)
+    _, l2, b2 = run_decode(inp, dev=dev)
+    assert np.array_equal(b1, b2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_page_permutation_is_bitwise_invariant(fmt):
+    inp = medium_inputs(fmt, q_len=2)
+    _, l1, b1 = run_decode(inp)
+    perm = np.random.default_rng(3).permutation(inp.num_pages)
+    inv = np.argsort(perm)
+    inp.k_cache, inp.v_cache = inp.k_cache[inv], inp.v_cache[inv]
+    if fmt == "fp8":
+        inp.k_scale, inp.v_scale = inp.k_scale[inv], inp.v_scale[inv]
+    bt = inp.block_table
+    inp.block_table = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    _, l2, b2 = run_decode(inp)
+    assert np.array_equal(b1, b2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_nan_poison_is_never_read(fmt):
+    clean = medium_inputs(fmt, q_len=3)
+    dirty = medium_inputs(fmt, q_len=3)
+    synth.apply_poison(dirty)
+    _, l1, b1 = run_decode(clean)
+    _, l2, b2 = run_decode(dirty)
+    assert np.array_equal(b1, b2) and np.array_equal(l1, l2)
+
+
+def test_v_all_ones_gives_exactly_one():
+    inp = medium_inputs("bf16")
+    inp.v_cache[:] = 0x3F80
+    out, _, _ = run_decode(inp, tile_tokens=256, num_workers=7)
+    assert (out == 1.0).all()
+
+
+def test_single_key_gives_v0_bit_exact():
+    inp = synth.make_inputs(cfg(), seed=2, seq_lens=[1] * 9)
+    _, _, bits = run_decode(inp)
+    G = inp.num_q_heads // inp.num_kv_heads
+    for b in range(inp.batch):
+        for h in range(inp.num_q_heads):
+            assert np.array_equal(bits[b, 0, h], inp.v_cache[inp.block_table[b, 0], h // G, 0])
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_equal_keys_give_mean_of_v(q_len):
+    inp = medium_inputs("bf16", q_len=q_len)
+    inp.k_cache[:] = inp.k_cache[0, 0, 0]
+    out, lse, _ = run_decode(inp, tile_tokens=128, num_workers=5)
+    check(inp, out, lse, tag="equal keys")
+
+
+def test_large_magnitude_scores():
+    inp = medium_inputs("bf16", q_len=2)
+    inp.q = synth.f32_to_bf16_bits((bf16_bits_to_f64(inp.q) * 30.0).astype(np.float32))
+    out, lse, _ = run_decode(inp)
+    ref_out, ref_lse = oracle.decode_attention(inp)
+    assert np.isfinite(out).all()
+    assert max_abs(out, ref_out) <= TOL["bf16"]
+    assert max_abs(lse, ref_lse) <= 30 * LSE_TOL     # lse scales with the scores
+
+
+def test_draft_rows_match_single_token_decodes():
+    sl = [4, 17, 33, 34, 35, 36, 100]
+    inp = synth.make_inputs(cfg(q_len=4), seed=8, seq_lens=sl)
+    out4, _, _ = run_decode(inp, tile_tokens=16, num_workers=3)
+    for t in range(4):
+        one = synth.make_inputs(cfg(q_len=1), seed=8, seq_lens=sl)
+        one.k_cache, one.v_cache, one.block_table = inp.k_cache, inp.v_cache, inp.block_table
+        one.q = inp.q[:, t:t + 1].copy()
+        one.seq_lens = (inp.seq_lens - 4 + t + 1).astype(np.int32)
+        out1, _, _ = run_decode(one, tile_tokens=16, num_workers=3)
+        assert max_abs(out4[:, t], out1[:, 0]) <= TOL["bf16"]
+
+
+def test_fp8_codes_decode_exactly():
+    """Every finite e4m3fn code read through the kernel's V path with one key and
+    scale 1 comes back as its exact value (decoded in bf16)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    inp = synth.make_inputs(cfg(kv_format="fp8", page_size=64, num_q_heads=1, num_kv_heads=1),
+                            seed=1, seq_lens=[1, 1])
+    inp.v_scale[:] = 1.0
+    flat = np.zeros(256, dtype=np.uint8)
+    flat[:len(codes)] = codes
+    for b in range(2):
+        inp.v_cache[inp.block_table[b, 0], 0, 0, :] = flat[128 * b:128 * (b + 1)]
+    out, _, _ = run_decode(inp)
+    got = out[:, 0, 0, :].reshape(-1)[:len(codes)]
+    assert np.array_equal(got, E4M3FN_TABLE[codes])
+
+
+@pytest.mark.parametrize("T,W", [(16, 1), (48, 13), (256, 512), (1024, 64), (4096, 2)])
+def test_tile_and_worker_sweep(T, W):
+    inp = medium_inputs("bf16", q_len=2)
+    out, lse, _ = run_decode(inp, tile_tokens=T, num_workers=W)
+    check(inp, out, lse, tag="T=%d W=%d" % (T, W))
+
+
+def test_combine_alone_matches_lse_merge():
+    import torch
+    import paged_kv_gqa_amd as pkv
+    rng = np.random.default_rng(4)
+    B, Tq, Hq, Hkv, D = 3, 2, 8, 2, 128
+    G, M = Hq // Hkv, (Hq // Hkv) * Tq
+    nb = np.array([1, 4, 9], dtype=np.int32)
+    rtb = np.concatenate([[0], np.cumsum(nb)]).astype(np.int32)
+    NP = int(Hkv * rtb[-1])
+    o = rng.standard_normal((NP, M, D)).astype(np.float32)
+    lse = (rng.standard_normal((NP, M)) * 3).astype(np.float32)
+    lse[5, 2] = -np.inf
+    nbytes = pkv.pkv_workspace_bytes(NP, M, D)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    obytes = NP * M * D * 4
+    ws[:obytes].copy_(torch.from_numpy(o.view(np.uint8).reshape(-1)))
+    off = (obytes + 255) // 256 * 256
+    ws[off:off + NP * M * 4].copy_(torch.from_numpy(lse.view(np.uint8).reshape(-1)))
+    out = torch.empty((B, Tq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    pkv.pkv_combine(workspace=ws, workspace_bytes=nbytes, num_partials=NP,
+                    req_tile_base=torch.from_numpy(rtb).cuda(), batch=B, q_len=Tq, num_q_heads=Hq,
+                    num_kv_heads=Hkv, head_dim=D, out=out, lse_out=lse_out)
+    torch.cuda.synchronize()
+    got, got_lse = out.float().cpu().numpy(), lse_out.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            for h in range(Hq):
+                g, r = h // G, t * G + h % G
+                slots = Hkv * rtb[b] + g * nb[b] + np.arange(nb[b])
+                ref, ref_l = oracle.lse_merge(o[slots, r], lse[slots, r])
+                assert np.all(np.abs(got[b, t, h] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+                assert abs(got_lse[b, t, h] - ref_l) <= 1e-5 * max(1.0, abs(ref_l))
+
+
+def test_empty_batch_is_a_no_op():
+    import torch
+    inp = synth.make_inputs(cfg(), seed=0, seq_lens=[5])
+    runner = make_runner(inp)
+    dev = device_inputs(inp)
+    out = runner(dev["q"][:0], dev["k"], dev["v"], dev["bt"][:0], np.zeros(0, np.int32), inp.scale)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 1, 8, 128)
