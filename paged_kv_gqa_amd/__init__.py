@@ -13,6 +13,10 @@ import ctypes
 import os
 
 import numpy as np
+# torch ships its own HIP runtime (soname libamdhip64.so.7). Loading it before the
+# library makes libpkv.so bind to that same runtime, so the process holds one HIP/HSA
+# runtime and torch's device pointers and streams are valid in the library.
+import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")

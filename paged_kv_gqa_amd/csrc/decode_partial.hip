@@ -158,7 +158,7 @@ __device__ __forceinline__ void load_chunk(Chunk<D, FP8>& ch, const uint8_t* __r
 template <int D, bool FP8>
 __device__ __forceinline__ void process_chunk(const Chunk<D, FP8>& ch, const u32x4 (&qf)[D / 32],
                                               const u32x4 (&sel)[2], f32x4 (&acc)[D / 16],
-                                              float& m, float& lsum, int j0, int lim,
+                                              float& m, float& lsum, float& lexact, int j0, int lim,
                                               int tile_end, float c_qk, float v_mul, int n,
                                               int gq) {
   using C = Cfg<D, FP8>;
@@ -214,16 +214,18 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, FP8>& ch, const u32
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(m - m_use);
   unsigned pk[4];
-  float psum = 0.f;
+  float psum = 0.f, pexact = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float p0 = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
     const float p1 = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
     const unsigned u = pack_bf16(p0, p1);
-    psum += bf16_lo(u) + bf16_hi(u);   // the row sum uses the rounded weights of P.V
+    psum += bf16_lo(u) + bf16_hi(u);   // normaliser: the rounded weights P.V sees
+    pexact += p0 + p1;                 // log-sum-exp: the unrounded weights
     pk[e] = FP8 ? pack_bf16(p0 * v_mul, p1 * v_mul) : u;
   }
   lsum = lsum * alpha + psum;
+  lexact = lexact * alpha + pexact;
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
     for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
@@ -265,6 +267,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   __shared__ float lds_o[kWaves][kMaxRows][kLdsStride];
   __shared__ float lds_m[kWaves][kMaxRows];
   __shared__ float lds_l[kWaves][kMaxRows];
+  __shared__ float lds_le[kWaves][kMaxRows];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     f32x4 acc[C::kBlocks];
 #pragma unroll
     for (int bl = 0; bl < C::kBlocks; ++bl) acc[bl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.f;
+    float m = -INFINITY, lsum = 0.f, lexact = 0.f;
 
     const int nchunks = (it.tile_end - it.tile_start + 31) >> 5;
     float c_qk = sh.qk_scale_log2, v_mul = 1.f;
@@ -353,14 +356,14 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
         const int c2 = c1 + kWaves;
         hoA = c2 < nchunks ? chunk_offsets(it, c2) : hoB;
         chunk_scales(c0);
-        process_chunk<D, FP8>(A, qf, sel, acc, m, lsum, it.tile_start + 32 * c0, lim, it.tile_end,
+        process_chunk<D, FP8>(A, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c0, lim, it.tile_end,
                               c_qk, v_mul, n, gq);
         if (c1 >= nchunks) break;
         load_chunk<D, FP8>(A, k_cache, v_cache, hoA, lane_off);
         const int c3 = c2 + kWaves;
         hoB = c3 < nchunks ? chunk_offsets(it, c3) : hoA;
         chunk_scales(c1);
-        process_chunk<D, FP8>(B, qf, sel, acc, m, lsum, it.tile_start + 32 * c1, lim, it.tile_end,
+        process_chunk<D, FP8>(B, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c1, lim, it.tile_end,
                               c_qk, v_mul, n, gq);
         if (c2 >= nchunks) break;
         c0 = c2;
@@ -368,12 +371,15 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       }
     }
 
-    // Wave result -> LDS: row max, full row sum, unnormalised O.
+    // Wave result -> LDS: row max, full row sums, unnormalised O.
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
+    lexact += __shfl_xor(lexact, 16);
+    lexact += __shfl_xor(lexact, 32);
     if (gq == 0) {
       lds_m[wid][n] = m;
       lds_l[wid][n] = lsum;
+      lds_le[wid][n] = lexact;
     }
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       if (mx != -INFINITY) {
         float den = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][tid] - mx) * lds_l[w][tid];
+        for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][tid] - mx) * lds_le[w][tid];
         lse = (mx + __builtin_amdgcn_logf(den)) * kLn2;
       }
       ws_lse[static_cast<int64_t>(slot) * M + tid] = lse;

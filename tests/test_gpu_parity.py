@@ -1,10 +1,14 @@
 """GPU parity of the HIP decode path against the fp64 oracle (needs an MI355X).
 
 Tolerances (the contract): max |gpu - oracle| <= 1e-2 on the bf16 output for BF16 KV
-and <= 3e-2 for FP8 KV, against the oracle on the same stored inputs. Tighter
-diagnostics are asserted too, because an absolute 1e-2 is loose at long L (outputs
-shrink like 1/sqrt(L)): relative L2 error <= 1e-2 and |lse - lse_ref| <= 1e-3. The
-arithmetic behind them: bf16 weights (relative 2^-9 each, averaging out), fp32
+and <= 3e-2 for FP8 KV, against the oracle on the same stored inputs. One exception
+is forced by the output format: a bf16 value of magnitude >= 4 has a spacing of
+2^-5, so rounding alone can move it 1.6e-2; there the bound is 0.6 bf16 ulp of the
+reference instead (elementwise tolerance max(tol, 0.6 * ulp_bf16(ref))).
+
+Tighter diagnostics are asserted too, because an absolute 1e-2 is loose at long L
+(outputs shrink like 1/sqrt(L)): relative L2 error <= 1e-2 and |lse - lse_ref| <= 1e-3.
+The arithmetic behind them: bf16 weights (relative 2^-9 each, averaging out), fp32
 accumulation, one bf16 rounding of the output (2^-9 relative).
 """
 
@@ -38,6 +42,18 @@ def cfg(**kw):
     return base
 
 
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    _, e = np.frexp(np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def excess(out, ref, tol):
+    """Largest amount by which |out - ref| exceeds the elementwise tolerance."""
+    err = np.abs(np.asarray(out, np.float64) - ref)
+    return float(np.max(err - np.maximum(tol, 0.6 * bf16_ulp(ref)), initial=-np.inf))
+
+
 def check(inp, out, lse, pairs=None, tag=""):
     ref_out, ref_lse = oracle.decode_attention(inp, pairs=pairs)
     if pairs is not None:
@@ -50,7 +66,7 @@ def check(inp, out, lse, pairs=None, tag=""):
     assert np.isfinite(out).all() and np.isfinite(lse).all(), tag
     ea, er, el = max_abs(out, ref_out), rel_l2(out, ref_out), max_abs(lse, ref_lse)
     log("  %s: max_abs %.3e rel_l2 %.3e lse %.3e" % (tag, ea, er, el))
-    assert ea <= TOL[inp.kv_format], tag
+    assert excess(out, ref_out, TOL[inp.kv_format]) <= 0, tag
     assert er <= REL_TOL, tag
     assert el <= LSE_TOL, tag
 
@@ -181,7 +197,7 @@ def test_large_magnitude_scores():
     out, lse, _ = run_decode(inp)
     ref_out, ref_lse = oracle.decode_attention(inp)
     assert np.isfinite(out).all()
-    assert max_abs(out, ref_out) <= TOL["bf16"]
+    assert excess(out, ref_out, TOL["bf16"]) <= 0
     assert max_abs(lse, ref_lse) <= 30 * LSE_TOL     # lse scales with the scores
 
 
@@ -195,7 +211,7 @@ def test_draft_rows_match_single_token_decodes():
         one.q = inp.q[:, t:t + 1].copy()
         one.seq_lens = (inp.seq_lens - 4 + t + 1).astype(np.int32)
         out1, _, _ = run_decode(one, tile_tokens=16, num_workers=3)
-        assert max_abs(out4[:, t], out1[:, 0]) <= TOL["bf16"]
+        assert excess(out4[:, t], out1[:, 0].astype(np.float64), TOL["bf16"]) <= 0
 
 
 def test_fp8_codes_decode_exactly():
