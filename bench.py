@@ -1,0 +1,203 @@
+"""Bench: paged-KV GQA split-KV decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixed] [--gpus 1]
+
+One step = the whole hot path over one decode batch: host plan (uniform tiles,
+greedy bin-packing), one H2D copy of the plan, the split-KV partial kernel and the
+log-sum-exp combine kernel, all on one stream. Inputs (seeded, synthetic) are
+resident in HBM before timing starts. Prints ONE JSON line on stdout; progress
+goes to stderr.
+
+value = algorithmic bytes / wall time per step (GB/s). Algorithmic bytes: K and V of
+every valid token, Q, the bf16 output, the block-table entries used, seq_lens and
+(FP8) the page scales; split-KV partials are excluded.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention achieved HBM GB/s (% of peak) + µs/step, mixed KV lengths"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
+KERNEL_SOURCES = ["paged_kv_gqa_amd/csrc/decode_partial.hip", "paged_kv_gqa_amd/csrc/kernels.hpp"]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode_partial launch from the committed counter summary, if it
+    was taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, algo_bytes):
+    """Time the fp64 CPU oracle on the same workload (one full step)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    log("cpu baseline: timing the oracle on the full batch")
+    t0 = time.perf_counter()
+    oracle.decode_attention(inp)
+    dt = time.perf_counter() - t0
+    return {"value": round(algo_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "one full step of the same workload (all %d requests x %d kv heads), "
+                      "fp64 numpy, host cores of the GPU box" % (inp.batch, inp.num_kv_heads),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed")
+    ap.add_argument("--tile-tokens", type=int, default=0)
+    ap.add_argument("--num-workers", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_gqa_amd as pkv
+
+    cfg = synth.ALL[args.workload]
+    log("generating %s inputs (seed %d)" % (args.workload, args.seed))
+    inp = synth.make_inputs(cfg, seed=args.seed)
+    algo = synth.algorithmic_bytes(inp)
+    out_bytes = inp.batch * inp.q_len * inp.num_q_heads * inp.head_dim * 2
+    partial_algo = algo - out_bytes          # what decode_partial itself must move
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if inp.kv_format == "bf16":
+        k = torch.from_numpy(inp.k_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(inp.v_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        k = torch.from_numpy(inp.k_cache).to(dev)
+        v = torch.from_numpy(inp.v_cache).to(dev)
+        ks = torch.from_numpy(inp.k_scale).to(dev)
+        vs = torch.from_numpy(inp.v_scale).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl_dev = torch.from_numpy(inp.seq_lens).to(dev)
+    seq_lens_h = inp.seq_lens.copy()
+    runner = pkv.PagedDecode(num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
+                             head_dim=inp.head_dim, page_size=inp.page_size,
+                             kv_format=inp.kv_format, q_len=inp.q_len,
+                             tile_tokens=args.tile_tokens, num_workers=args.num_workers)
+    out = torch.empty((inp.batch, inp.q_len, inp.num_q_heads, inp.head_dim), dtype=torch.bfloat16,
+                      device=dev)
+
+    def step(events=None):
+        runner(q, k, v, bt, seq_lens_h, inp.scale, k_scale=ks, v_scale=vs, seq_lens=sl_dev,
+               out=out, partial_events=events)
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan = runner.last_plan
+    log("plan: tile %d tokens, %d items, %d workers" % (plan["T"], plan["N"], plan["W"]))
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall / K * 1e3
+    value = algo / (wall / K) / 1e9
+    achieved = partial_algo / kern_avg_s / 1e9
+    traffic = measured_traffic(args.workload)
+    log("%.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s); decode_partial %.1f us avg (%.1f GB/s)" % (
+        ms_per_step * 1e3, value, 100 * value / HBM_PEAK_GBS, kern_avg_s * 1e6, achieved))
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.kv_format,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg["desc"],
+            "batch": inp.batch,
+            "sum_seq_lens": int(inp.seq_lens.sum()),
+            "q_len": inp.q_len,
+            "heads": "%d q / %d kv" % (inp.num_q_heads, inp.num_kv_heads),
+            "head_dim": inp.head_dim,
+            "page_size": inp.page_size,
+            "tile_tokens": plan["T"],
+            "work_items": plan["N"],
+            "num_workers": plan["W"],
+            "algorithmic_bytes_per_step": algo,
+            "step": "host plan + plan H2D + decode_partial + combine",
+        },
+        "roofline": {
+            "kernel": "decode_partial",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": partial_algo,
+            "avg_launch_us": round(kern_avg_s * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, algo)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -298,9 +298,16 @@ class PagedDecode:
         return self._workspace, nbytes
 
     def __call__(self, q, k_cache, v_cache, block_table, seq_lens_h, scale, *, k_scale=None,
-                 v_scale=None, seq_lens=None, out=None, lse_out=None, stream=None):
+                 v_scale=None, seq_lens=None, out=None, lse_out=None, stream=None,
+                 partial_events=None):
         """Run one decode step. ``seq_lens_h`` (host ints) drives the plan; ``seq_lens``
-        (device int32) defaults to a copy uploaded with the plan."""
+        (device int32) defaults to a copy uploaded with the plan. ``partial_events``: two
+        torch.cuda.Events recorded around the decode_partial launch (for timing)."""
+        if stream is not None:
+            with self.torch.cuda.stream(stream):
+                return self(q, k_cache, v_cache, block_table, seq_lens_h, scale, k_scale=k_scale,
+                            v_scale=v_scale, seq_lens=seq_lens, out=out, lse_out=lse_out,
+                            partial_events=partial_events)
         torch = self.torch
         p = self.plan(seq_lens_h)
         items, offs, rtb, sl_dev = self.upload(p)
@@ -311,6 +318,8 @@ class PagedDecode:
         if out is None:
             out = torch.empty((B, self.q_len, self.num_q_heads, self.head_dim), dtype=torch.bfloat16,
                               device=self.device)
+        if partial_events is not None:
+            partial_events[0].record()
         pkv_decode_partial(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
                            seq_lens=seq_lens, items=items, worker_offsets=offs, req_tile_base=rtb,
                            workspace=ws, workspace_bytes=ws_bytes, num_items=p["N"],
@@ -319,11 +328,12 @@ class PagedDecode:
                            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
                            page_size=self.page_size, bt_stride=block_table.shape[1],
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
-                           scale=scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
+                           scale=scale, k_scale=k_scale, v_scale=v_scale)
+        if partial_events is not None:
+            partial_events[1].record()
         pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"], req_tile_base=rtb,
                     batch=B, q_len=self.q_len, num_q_heads=self.num_q_heads,
-                    num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, out=out, lse_out=lse_out,
-                    stream=stream)
+                    num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, out=out, lse_out=lse_out)
         return out
 
 

@@ -1,10 +1,13 @@
 // Log-sum-exp merge of split-KV partials (the combine kernel of the HPC-Ops review,
 // "How the kernels are organized around specific workload shapes").
 //
-// One wave per output row (b, t, h); each lane owns D/64 head dimensions. The
-// n_b partials of the row are read in index order with a running maximum, so the
-// result is deterministic. A request with a single tile still passes through here
-// (the partial is already normalised; the merge only casts it to bf16).
+// One wave per output row (b, t, h). The row's n_b split weights are computed in
+// parallel, one split per lane: lane i reads lse_i, the wave takes the maximum and
+// each lane forms w_i = exp(lse_i - max). The partial outputs are then accumulated
+// in split order with the weights broadcast from their lanes; their loads do not
+// depend on each other, so several are in flight at once. Fixed summation order
+// keeps the result deterministic. A request with a single tile still passes through
+// here (its partial is already normalised; the merge only casts it to bf16).
 #include "kernels.hpp"
 
 #include <math.h>
@@ -18,6 +21,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kRowsPerBlock = 4;
+constexpr int kUnroll = 8;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
 
 template <int D>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const CombineParams p) {
@@ -34,35 +50,53 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
   const int base = p.req_tile_base[b];
   const int nb = p.req_tile_base[b + 1] - base;
   const int64_t slot0 = static_cast<int64_t>(p.num_kv_heads) * base + static_cast<int64_t>(g) * nb;
+  const float* lse = p.ws_lse + slot0 * p.rows + r;           // stride rows per split
+  const float* o = p.ws_o + (slot0 * p.rows + r) * D + E * lane;  // stride rows * D per split
+  const int64_t ostride = static_cast<int64_t>(p.rows) * D;
 
-  float mrun = -INFINITY, den = 0.f;
+  float mloc = -INFINITY;
+  for (int i = lane; i < nb; i += 64) mloc = fmaxf(mloc, lse[static_cast<int64_t>(i) * p.rows]);
+  const float mx = wave_max(mloc) * kLog2e;  // -inf only if every split saw no key
+  const float m_use = (mx == -INFINITY) ? 0.f : mx;
+
+  float den = 0.f;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nb; ++i) {
-    const int64_t rr = (slot0 + i) * p.rows + r;
-    const float li = p.ws_lse[rr] * kLog2e;
-    float o[E];
-    if constexpr (E == 2) {
-      const f32x2 v = *reinterpret_cast<const f32x2*>(p.ws_o + rr * D + 2 * lane);
-      o[0] = v[0];
-      o[1] = v[1];
-    } else {
-      o[0] = p.ws_o[rr * D + lane];
-    }
-    if (li == -INFINITY) continue;
-    if (li > mrun) {
-      const float sc = __builtin_amdgcn_exp2f(mrun - li);  // 0 when mrun = -inf
-      den *= sc;
+  for (int i0 = 0; i0 < nb; i0 += 64) {
+    const int i = i0 + lane;
+    const float wl = (i < nb) ? __builtin_amdgcn_exp2f(lse[static_cast<int64_t>(i) * p.rows] * kLog2e - m_use) : 0.f;
+    den += wl;
+    const int cnt = min(64, nb - i0);
+    int j = 0;
+    for (; j + kUnroll <= cnt; j += kUnroll) {
+      float ov[kUnroll][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] *= sc;
-      mrun = li;
-    }
-    const float w = __builtin_amdgcn_exp2f(li - mrun);
-    den += w;
+      for (int u = 0; u < kUnroll; ++u) {
+        const float* src = o + (i0 + j + u) * ostride;
+        if constexpr (E == 2) {
+          const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+          ov[u][0] = v[0];
+          ov[u][1] = v[1];
+        } else {
+          ov[u][0] = *src;
+        }
+      }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += w * o[e];
+      for (int u = 0; u < kUnroll; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += w * ov[u][e];
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+      const float* src = o + (i0 + j) * ostride;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * src[e];
+    }
   }
+  den = wave_sum(den);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint16_t* orow = p.out + static_cast<int64_t>(row) * D;
   if constexpr (E == 2) {
@@ -72,7 +106,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
     orow[lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[0] * inv));
   }
   if (p.lse_out != nullptr && lane == 0)
-    p.lse_out[row] = den > 0.f ? (mrun + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+    p.lse_out[row] = den > 0.f ? (m_use + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

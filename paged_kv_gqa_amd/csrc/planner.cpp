@@ -5,14 +5,12 @@
 // first; with all loads starting equal, the k-th full tile in (b, g, i) order lands
 // on worker k mod W (each is the lowest-indexed least-loaded worker at its turn).
 // Only the at most B*Hkv partial tiles (one per request and kv head) go through a
-// (load, worker) min-heap, longest first, ties by (b, g).
+// (load, worker) tournament tree, longest first, ties by (b, g).
 #include "planner.hpp"
 
 #include <algorithm>
-#include <functional>
+#include <cstdint>
 #include <numeric>
-#include <queue>
-#include <utility>
 
 namespace pkv {
 
@@ -20,50 +18,78 @@ namespace {
 
 constexpr int64_t kMaxAutoTile = 4096;
 
-struct Partial {
-  int64_t cost;
-  int32_t b, g;
+// Tournament tree over the workers' loads. A key packs (load, worker) into one
+// 64-bit word, load in the high bits, so the smaller key is the less-loaded worker
+// and, on equal loads, the lower index. Leaves hold the workers' keys, every inner
+// node the smaller key of its children; raising the least-loaded worker's load
+// re-plays its fixed-depth path to the root with one min per level.
+class WorkerTree {
+ public:
+  static constexpr int kWorkerBits = 24;  // up to 16M workers; loads below 2^40 tokens
+  void reset(const std::vector<int64_t>& loads) {
+    const int W = static_cast<int>(loads.size());
+    size_ = 1;
+    while (size_ < W) size_ *= 2;
+    node_.assign(2 * size_, UINT64_MAX);  // padding leaves never win
+    for (int w = 0; w < W; ++w)
+      node_[size_ + w] = (static_cast<uint64_t>(loads[w]) << kWorkerBits) | static_cast<uint64_t>(w);
+    for (int i = size_ - 1; i >= 1; --i) node_[i] = std::min(node_[2 * i], node_[2 * i + 1]);
+  }
+  // Add `cost` to the least-loaded worker (lowest index on ties); returns it.
+  int32_t place(int64_t cost) {
+    const uint64_t top = node_[1];
+    const int32_t w = static_cast<int32_t>(top & ((uint64_t{1} << kWorkerBits) - 1));
+    int i = size_ + w;
+    node_[i] = top + (static_cast<uint64_t>(cost) << kWorkerBits);
+    for (i >>= 1; i >= 1; i >>= 1) node_[i] = std::min(node_[2 * i], node_[2 * i + 1]);
+    return w;
+  }
+
+ private:
+  int size_ = 1;
+  std::vector<uint64_t> node_;
 };
 
-// Partial tiles of the plan in placement order.
-std::vector<Partial> partial_tiles(int batch, const int32_t* seq_lens, int Hkv, int64_t T) {
-  std::vector<Partial> out;
-  for (int b = 0; b < batch; ++b) {
-    const int64_t rem = seq_lens[b] % T;
-    if (rem == 0) continue;
-    for (int g = 0; g < Hkv; ++g) out.push_back({rem, b, g});
-  }
-  std::stable_sort(out.begin(), out.end(),
-                   [](const Partial& x, const Partial& y) { return x.cost > y.cost; });
-  return out;
-}
+struct Scratch {
+  std::vector<int64_t> loads, counts, full;
+  std::vector<int32_t> reqs, nfull, rem;  // per request: full tiles, last-tile tokens
+  WorkerTree heap;
+};
 
-int64_t full_tile_count(int batch, const int32_t* seq_lens, int Hkv, int64_t T) {
+// Per-request tile counts for tile size T; returns the number of full tiles of one
+// kv head. Divisions happen once per request here and nowhere in the loops below.
+int64_t split_requests(int batch, const int32_t* seq_lens, int64_t T, Scratch& s) {
+  s.nfull.resize(batch);
+  s.rem.resize(batch);
   int64_t f = 0;
-  for (int b = 0; b < batch; ++b) f += seq_lens[b] / T;
-  return f * Hkv;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t q = static_cast<int32_t>(seq_lens[b] / T);
+    s.nfull[b] = q;
+    s.rem[b] = seq_lens[b] - static_cast<int32_t>(q * T);
+    f += q;
+  }
+  return f;
 }
 
-using Slot = std::pair<int64_t, int32_t>;  // (load, worker)
-using MinHeap = std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>>;
+void partial_requests(int batch, Scratch& s) {
+  s.reqs.clear();
+  for (int b = 0; b < batch; ++b)
+    if (s.rem[b] != 0) s.reqs.push_back(b);
+  const int32_t* rem = s.rem.data();
+  std::stable_sort(s.reqs.begin(), s.reqs.end(),
+                   [rem](int32_t x, int32_t y) { return rem[x] > rem[y]; });
+}
 
-// Place the partial tiles; returns the worker of each, and updates loads / counts.
-std::vector<int32_t> place_partials(const std::vector<Partial>& parts, int W,
-                                    std::vector<int64_t>& loads,
-                                    std::vector<int64_t>& counts) {
-  std::vector<Slot> init(W);
-  for (int w = 0; w < W; ++w) init[w] = {loads[w], w};
-  MinHeap heap(std::greater<Slot>(), std::move(init));
-  std::vector<int32_t> where(parts.size());
-  for (size_t k = 0; k < parts.size(); ++k) {
-    Slot s = heap.top();
-    heap.pop();
-    where[k] = s.second;
-    loads[s.second] = s.first + parts[k].cost;
-    counts[s.second] += 1;
-    heap.push({loads[s.second], s.second});
+// Full-tile phase: loads and counts after round-robin placement.
+void full_phase(int64_t F, int64_t T, int W, Scratch& s) {
+  s.full.assign(W, 0);
+  s.loads.resize(W);
+  s.counts.resize(W);
+  for (int w = 0; w < W; ++w) {
+    s.full[w] = F / W + (w < F % W ? 1 : 0);
+    s.counts[w] = s.full[w];
+    s.loads[w] = s.full[w] * T;
   }
-  return where;
 }
 
 }  // namespace
@@ -73,20 +99,35 @@ int64_t tile_quantum(int page_size, bool fp8) {
   return static_cast<int64_t>(page_size) * 64 / std::gcd(page_size, 64);
 }
 
-PlanStats plan_stats(int batch, const int32_t* seq_lens, int Hkv, int64_t T, int W) {
-  const int64_t F = full_tile_count(batch, seq_lens, Hkv, T);
-  std::vector<int64_t> counts(W), loads(W);
-  for (int w = 0; w < W; ++w) {
-    counts[w] = F / W + (w < F % W ? 1 : 0);
-    loads[w] = counts[w] * T;
+namespace {
+
+// Expects split_requests(T) to have filled s.nfull / s.rem.
+PlanStats plan_stats_impl(int batch, int Hkv, int64_t T, int W, int64_t full_one_head, Scratch& s) {
+  const int64_t F = full_one_head * Hkv;
+  full_phase(F, T, W, s);
+  partial_requests(batch, s);
+  s.heap.reset(s.loads);
+  for (int32_t b : s.reqs) {
+    const int64_t cost = s.rem[b];
+    for (int g = 0; g < Hkv; ++g) {
+      const int32_t w = s.heap.place(cost);
+      s.loads[w] += cost;
+      s.counts[w] += 1;
+    }
   }
-  const std::vector<Partial> parts = partial_tiles(batch, seq_lens, Hkv, T);
-  place_partials(parts, W, loads, counts);
   PlanStats st;
-  st.num_items = F + static_cast<int64_t>(parts.size());
-  st.makespan = *std::max_element(loads.begin(), loads.end());
-  st.max_items = *std::max_element(counts.begin(), counts.end());
+  st.num_items = F + static_cast<int64_t>(s.reqs.size()) * Hkv;
+  st.makespan = *std::max_element(s.loads.begin(), s.loads.end());
+  st.max_items = *std::max_element(s.counts.begin(), s.counts.end());
   return st;
+}
+
+}  // namespace
+
+PlanStats plan_stats(int batch, const int32_t* seq_lens, int Hkv, int64_t T, int W) {
+  Scratch s;
+  const int64_t f = split_requests(batch, seq_lens, T, s);
+  return plan_stats_impl(batch, Hkv, T, W, f, s);
 }
 
 int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_q_heads,
@@ -94,16 +135,53 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
   const int64_t quantum = tile_quantum(page_size, fp8);
   const int64_t eb = fp8 ? 1 : 2;
   const int64_t M = static_cast<int64_t>(num_q_heads / Hkv) * q_len;
-  int64_t best_T = quantum, best_est = -1;
+  const int64_t item_cost = M * (head_dim + 1) * 4;
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) total += seq_lens[b];
+  total *= Hkv;
+  std::vector<int64_t> cands;
   for (int64_t T = quantum;; T *= 2) {
-    const PlanStats st = plan_stats(batch, seq_lens, Hkv, T, W);
-    const int64_t est = st.makespan * 2 * head_dim * eb +
-                        (st.max_items + ceil_div(st.num_items, W)) * M * (head_dim + 1) * 4;
-    if (best_est < 0 || est <= best_est) {  // ascending T: ties go to the larger tile
+    cands.push_back(T);
+    if (T * 2 > kMaxAutoTile) break;
+  }
+  // Largest tile first, so a tie keeps the larger tile by strict improvement only.
+  // A candidate whose lower bound (perfect balance, ceil(N/W) items per worker) is
+  // not below the best estimate cannot win and is not simulated.
+  // Candidates are quantum * 2^k, so floor(L / T) = floor(L / quantum) >> k.
+  Scratch s;
+  std::vector<int32_t> lq(batch), lr(batch);
+  for (int b = 0; b < batch; ++b) {
+    lq[b] = static_cast<int32_t>(seq_lens[b] / quantum);
+    lr[b] = seq_lens[b] - static_cast<int32_t>(lq[b] * quantum);
+  }
+  s.nfull.resize(batch);
+  s.rem.resize(batch);
+  int64_t best_T = cands.back(), best_est = -1;
+  for (int k = static_cast<int>(cands.size()) - 1; k >= 0; --k) {
+    const int64_t T = cands[k];
+    int64_t f = 0, partial = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int32_t q = lq[b] >> k;
+      s.nfull[b] = q;
+      s.rem[b] = seq_lens[b] - static_cast<int32_t>(q * T);
+      f += q;
+      partial += (s.rem[b] != 0);
+    }
+    const int64_t n_items = (f + partial) * Hkv;
+    const int64_t per_worker = ceil_div(n_items, W);
+    // Lower bounds: the loads and item counts after the exact full-tile phase only
+    // grow, and no plan beats perfect balance.
+    const int64_t full_per_worker = ceil_div(f * Hkv, W);
+    const int64_t span_lb = std::max(ceil_div(total, W), full_per_worker * T);
+    const int64_t lower = span_lb * 2 * head_dim * eb +
+                          (std::max(per_worker, full_per_worker) + per_worker) * item_cost;
+    if (best_est >= 0 && lower >= best_est) continue;  // cannot improve strictly
+    const PlanStats st = plan_stats_impl(batch, Hkv, T, W, f, s);
+    const int64_t est = st.makespan * 2 * head_dim * eb + (st.max_items + per_worker) * item_cost;
+    if (best_est < 0 || est < best_est) {
       best_T = T;
       best_est = est;
     }
-    if (T * 2 > kMaxAutoTile) break;
   }
   return best_T;
 }
@@ -114,19 +192,25 @@ void build_plan(int batch, const int32_t* seq_lens, int Hkv, int64_t T, int W,
   for (int b = 0; b < batch; ++b)
     req_tile_base[b + 1] = req_tile_base[b] + static_cast<int32_t>(ceil_div(seq_lens[b], T));
 
-  const int64_t F = full_tile_count(batch, seq_lens, Hkv, T);
-  std::vector<int64_t> full(W), counts(W), loads(W);
-  for (int w = 0; w < W; ++w) {
-    full[w] = F / W + (w < F % W ? 1 : 0);
-    counts[w] = full[w];
-    loads[w] = full[w] * T;
+  Scratch s;
+  const int64_t F = split_requests(batch, seq_lens, T, s) * Hkv;
+  full_phase(F, T, W, s);
+  partial_requests(batch, s);
+  s.heap.reset(s.loads);
+  std::vector<int32_t> where;
+  where.reserve(s.reqs.size() * Hkv);
+  for (int32_t b : s.reqs) {
+    const int64_t cost = s.rem[b];
+    for (int g = 0; g < Hkv; ++g) {
+      const int32_t w = s.heap.place(cost);
+      s.counts[w] += 1;
+      where.push_back(w);
+    }
   }
-  const std::vector<Partial> parts = partial_tiles(batch, seq_lens, Hkv, T);
-  const std::vector<int32_t> where = place_partials(parts, W, loads, counts);
 
   worker_offsets[0] = 0;
   for (int w = 0; w < W; ++w)
-    worker_offsets[w + 1] = worker_offsets[w] + static_cast<int32_t>(counts[w]);
+    worker_offsets[w + 1] = worker_offsets[w] + static_cast<int32_t>(s.counts[w]);
 
   auto put = [&](int64_t pos, int32_t b, int32_t g, int32_t i) {
     const int32_t nb = req_tile_base[b + 1] - req_tile_base[b];
@@ -136,19 +220,27 @@ void build_plan(int batch, const int32_t* seq_lens, int Hkv, int64_t T, int W,
     it[2] = i;
     it[3] = Hkv * req_tile_base[b] + g * nb + i;
   };
-  // Full tiles: the k-th in (b, g, i) order is worker (k mod W)'s (k / W)-th item.
-  int64_t k = 0;
+  // Full tiles: the k-th in (b, g, i) order is worker (k mod W)'s (k / W)-th item;
+  // (w, round) track (k mod W, k / W) without dividing.
+  int32_t w = 0, round = 0;
   for (int b = 0; b < batch; ++b) {
-    const int32_t nf = static_cast<int32_t>(seq_lens[b] / T);
+    const int32_t nf = s.nfull[b];
     for (int g = 0; g < Hkv; ++g)
-      for (int32_t i = 0; i < nf; ++i, ++k) put(worker_offsets[k % W] + k / W, b, g, i);
+      for (int32_t i = 0; i < nf; ++i) {
+        put(static_cast<int64_t>(worker_offsets[w]) + round, b, g, i);
+        if (++w == W) {
+          w = 0;
+          ++round;
+        }
+      }
   }
   // Partial tiles follow each worker's full tiles, in placement order.
-  std::vector<int64_t> cursor(W);
-  for (int w = 0; w < W; ++w) cursor[w] = worker_offsets[w] + full[w];
-  for (size_t p = 0; p < parts.size(); ++p) {
-    const int32_t b = parts[p].b;
-    put(cursor[where[p]]++, b, parts[p].g, static_cast<int32_t>(seq_lens[b] / T));
+  std::vector<int64_t>& cursor = s.loads;  // reused as per-worker write positions
+  for (int w = 0; w < W; ++w) cursor[w] = worker_offsets[w] + s.full[w];
+  size_t p = 0;
+  for (int32_t b : s.reqs) {
+    const int32_t last = s.nfull[b];
+    for (int g = 0; g < Hkv; ++g, ++p) put(cursor[where[p]]++, b, g, last);
   }
 }
 
