@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -194,6 +197,15 @@ def main():
             "avg_launch_us": round(kern_avg_s * 1e6, 2),
         },
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read and written" % n)
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, algo)
     print(json.dumps(rec), flush=True)
