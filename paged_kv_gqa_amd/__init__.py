@@ -229,14 +229,19 @@ def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batc
 
 class PagedDecode:
     """One decode step = host plan + one H2D copy of the plan + decode_partial + combine,
-    all enqueued on the current torch stream with no host synchronisation.
+    enqueued on the current torch stream with no host synchronisation.
 
-    Pinned plan buffers are used round-robin and each is reused only after the copy
-    that read it has completed. Device buffers (plan, workspace) grow on demand and
-    are kept, so after the first step no allocation happens at a fixed shape."""
+    With ``side_stream_upload`` the plan copy runs on a side stream, so it overlaps
+    the previous step's kernels, and the current stream waits for it (an event)
+    before decode_partial; otherwise it is enqueued on the current stream. Plans go
+    through rings of pinned and device buffers: a pinned buffer is rewritten only
+    after the copy that read it has completed, a device buffer only after the
+    kernels that read it have completed. Buffers grow on demand and are kept, so at
+    a fixed shape no allocation happens after the first steps."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
-                 q_len=1, tile_tokens=0, num_workers=0, device=None, pinned_slots=3):
+                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3,
+                 side_stream_upload=False):
         import torch
         self.torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
@@ -245,15 +250,17 @@ class PagedDecode:
         self.q_len, self.tile_tokens = q_len, tile_tokens
         self.rows = (num_q_heads // num_kv_heads) * q_len
         self.num_workers = num_workers or pkv_default_num_workers(self.device.index, kv_format, head_dim)
-        self._pinned = [None] * pinned_slots
-        self._events = [None] * pinned_slots
+        self._pinned = [None] * slots
+        self._dev = [None] * slots
+        self._copied = [None] * slots      # event on the copy stream: copy out of slot done
+        self._consumed = [None] * slots    # event on the compute stream: kernels reading slot done
         self._slot = 0
-        self._dev_plan = None
+        self._copy_stream = torch.cuda.Stream(device=self.device) if side_stream_upload else None
         self._workspace = None
         self.last_plan = None
 
     def plan(self, seq_lens_h):
-        """Host plan into a pinned buffer; returns a dict describing it."""
+        """Host plan into the next pinned buffer; returns a dict describing it."""
         torch = self.torch
         sl = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
         T, N, NP = pkv_plan_query(sl, self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim,
@@ -265,8 +272,8 @@ class PagedDecode:
         total = n_sl + _round4(B)
         k = self._slot
         self._slot = (k + 1) % len(self._pinned)
-        if self._events[k] is not None:
-            self._events[k].synchronize()          # the copy that last read this buffer is done
+        if self._copied[k] is not None:
+            self._copied[k].synchronize()          # the copy that last read this buffer is done
         buf = self._pinned[k]
         if buf is None or buf.numel() < total:
             buf = torch.empty(max(total, 1024), dtype=torch.int32, pin_memory=True)
@@ -280,20 +287,32 @@ class PagedDecode:
         return p
 
     def upload(self, p):
+        """Copy the plan on the side stream; make the current stream wait for it."""
         torch = self.torch
-        if self._dev_plan is None or self._dev_plan.numel() < p["total"]:
-            self._dev_plan = torch.empty(max(p["total"], 1024), dtype=torch.int32, device=self.device)
-        self._dev_plan[:p["total"]].copy_(self._pinned[p["slot"]][:p["total"]], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self._events[p["slot"]] = ev
-        d = self._dev_plan
-        return (d[:p["n_off"]], d[p["n_off"]:p["n_rtb"]], d[p["n_rtb"]:p["n_sl"]],
-                d[p["n_sl"]:p["n_sl"] + p["B"]])
+        k, total = p["slot"], p["total"]
+        main = torch.cuda.current_stream(self.device)
+        dev = self._dev[k]
+        if dev is None or dev.numel() < total:
+            torch.cuda.synchronize(self.device)    # rare: no kernel may still read the old buffer
+            dev = torch.empty(max(total, 1024), dtype=torch.int32, device=self.device)
+            self._dev[k] = dev
+        cs = self._copy_stream or main
+        if self._copy_stream is not None and self._consumed[k] is not None:
+            cs.wait_event(self._consumed[k])
+        with torch.cuda.stream(cs):
+            dev[:total].copy_(self._pinned[k][:total], non_blocking=True)
+            if self._copied[k] is None:
+                self._copied[k] = torch.cuda.Event()
+            self._copied[k].record(cs)
+        if self._copy_stream is not None:
+            main.wait_event(self._copied[k])
+        return (dev[:p["n_off"]], dev[p["n_off"]:p["n_rtb"]], dev[p["n_rtb"]:p["n_sl"]],
+                dev[p["n_sl"]:p["n_sl"] + p["B"]])
 
     def workspace(self, num_partials):
         nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)
         if self._workspace is None or self._workspace.numel() < nbytes:
+            self.torch.cuda.synchronize(self.device)
             self._workspace = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
         return self._workspace, nbytes
 
@@ -334,6 +353,10 @@ class PagedDecode:
         pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"], req_tile_base=rtb,
                     batch=B, q_len=self.q_len, num_q_heads=self.num_q_heads,
                     num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, out=out, lse_out=lse_out)
+        k = p["slot"]
+        if self._consumed[k] is None:
+            self._consumed[k] = torch.cuda.Event()
+        self._consumed[k].record()
         return out
 
 

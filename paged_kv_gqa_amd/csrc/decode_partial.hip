@@ -16,18 +16,23 @@
 //   hardware, re-derived for MFMA). Lane l owns query row n = l % 16 for the whole
 //   softmax, so row max, row sum and rescale factors never leave the lane except
 //   for one exchange across the four 16-lane groups.
-// - K and V are read straight from HBM with 16-byte loads in their natural
-//   [page][head][token][d] layout: lane l reads token (l % 16) of a half, bytes
-//   16*(l/16) + 64*u of its row, exactly the MFMA A-operand layout. QK^T needs no
-//   shuffling. P.V contracts over tokens, so V is transposed on the matrix core: an
-//   MFMA of the V half against a 0/1 selection matrix returns, in each lane, four
-//   consecutive tokens of one head dimension - the operand layout P.V needs -
-//   exactly (products by 1 and sums of zeros), in fp32, then packed back to bf16.
+// - K and V stream from HBM with non-temporal 16-byte loads, each wave instruction
+//   reading 1 KB of whole 128-byte lines of a 16-token half: on MI355X only
+//   full-line non-temporal reads reach ~6.8 TB/s on a random 4 KB page gather
+//   (half-line or cached reads stop near 6.1 TB/s). Each wave stages its chunk in
+//   its own LDS region (XOR-swizzled 16-byte units, so the reads below hit distinct
+//   banks) and reads it back in the MFMA operand layout: lane l holds token l % 16 of
+//   a half, bytes 16*(l/16) + 64*u of its row. QK^T then needs no shuffling. P.V
+//   contracts over tokens, so V is transposed on the matrix core: an MFMA of the V
+//   half against a 0/1 selection matrix returns, in each lane, four consecutive
+//   tokens of one head dimension - the operand layout P.V needs - exactly (products
+//   by 1 and sums of zeros), in fp32, then packed back to bf16.
 // - FP8 (OCP e4m3fn) K/V bytes are widened to bf16 with the gfx950 conversion
 //   instruction (exact). The per-(page, kv head) scales are applied outside the
 //   products: the K scale multiplies the scores, the V scale multiplies P before P.V.
-// - The next chunk's loads are issued before the current chunk is computed, so each
-//   wave keeps 16 KB (bf16) of KV in flight while its matrix and vector work runs.
+// - The next chunk's loads are issued into the same registers as soon as the
+//   current chunk sits in LDS, so each wave keeps one chunk (16 KB for bf16) in
+//   flight while its matrix and vector work runs.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -85,6 +90,12 @@ struct Cfg {
   static constexpr int kLoads = D * kEb / 64;     // 16-byte loads per lane per half
   static constexpr int kBlocks = D / 16;          // 16-wide head-dim blocks of the output
   static constexpr int kRowBytes = D * kEb;
+  static constexpr int kUnits = kRowBytes / 16;   // 16-byte units per token row
+  // Rows per 256 bytes is a power of two; the swizzle uses rows / (256 / kRowBytes).
+  static constexpr int kRowShift = kRowBytes == 256 ? 0 : (kRowBytes == 128 ? 1 : 2);
+  // Per-wave LDS: K and V stage (2 x 32 rows) or the wave's epilogue rows, whichever
+  // is larger, in 16-byte units.
+  static constexpr int kStageVec = 2 * 32 * kUnits > 4 * D ? 2 * 32 * kUnits : 4 * D;
 };
 
 // Head-dimension index that k-step s, lane group gq, element e of an MFMA operand
@@ -102,12 +113,6 @@ __device__ __forceinline__ int out_dim(int s, int c, int gq, int v) {
   const int k = 16 * c + 4 * gq + v;
   return op_dim<FP8>(s, k >> 3, k & 7);
 }
-
-template <int D, bool FP8>
-struct Chunk {
-  u32x4 k[2][Cfg<D, FP8>::kLoads];
-  u32x4 v[2][Cfg<D, FP8>::kLoads];
-};
 
 struct ItemCtx {
   const int32_t* __restrict__ bt;  // block-table row of the request
@@ -137,18 +142,75 @@ __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chun
   return r;
 }
 
+// One chunk as loaded: [K/V][half][instruction], 16 bytes per lane each.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_chunk(Chunk<D, FP8>& ch, const uint8_t* __restrict__ kc,
-                                           const uint8_t* __restrict__ vc, const HalfOffsets& ho,
-                                           int lane_off) {
+struct Raw {
+  u32x4 r[2][2][Cfg<D, FP8>::kLoads];
+};
+
+// Issue the chunk's loads: instruction j of half h reads bytes j*1024 + 16*lane of
+// the half's contiguous 16-row run (whole cache lines, non-temporal).
+template <int D, bool FP8>
+__device__ __forceinline__ void load_raw(Raw<D, FP8>& raw, const uint8_t* __restrict__ kc,
+                                         const uint8_t* __restrict__ vc, const HalfOffsets& ho,
+                                         int lane) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < Cfg<D, FP8>::kLoads; ++j) {
+      const int64_t off = ho.off[h] + j * 1024 + lane * 16;
+      raw.r[0][h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + off));
+      raw.r[1][h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + off));
+    }
+  }
+}
+
+// Stage slot of 16-byte unit `unit` of chunk row `row` (0..31) of K (kv 0) or V (1).
+// The unit index is XOR-ed with the row's position among the rows that share a
+// 256-byte bank window, so 16 lanes reading one unit column of 16 rows hit 16
+// distinct 16-byte bank groups.
+template <int D, bool FP8>
+__device__ __forceinline__ int stage_slot(int kv, int row, int unit) {
+  using C = Cfg<D, FP8>;
+  return (kv * 32 + row) * C::kUnits + (unit ^ ((row >> C::kRowShift) & (C::kUnits - 1)));
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_write(u32x4* __restrict__ st, const Raw<D, FP8>& raw, int lane) {
+  using C = Cfg<D, FP8>;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        const int pos = j * 1024 + lane * 16;
+        st[stage_slot<D, FP8>(kv, 16 * h + pos / C::kRowBytes, (pos % C::kRowBytes) / 16)] = raw.r[kv][h][j];
+      }
+}
+
+// Read the chunk back in MFMA operand layout: lane (n, gq) takes, for each half and
+// 16-byte piece u, bytes 64u + 16gq of token row n; fp8 pieces widen to two bf16
+// operand steps.
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_read(const u32x4* __restrict__ st, u32x4 (&kop)[2][D / 32],
+                                           u32x4 (&vop)[2][D / 32], int n, int gq) {
   using C = Cfg<D, FP8>;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int64_t off = ho.off[h] + lane_off;
 #pragma unroll
     for (int u = 0; u < C::kLoads; ++u) {
-      ch.k[h][u] = *reinterpret_cast<const u32x4*>(kc + off + 64 * u);
-      ch.v[h][u] = *reinterpret_cast<const u32x4*>(vc + off + 64 * u);
+      const u32x4 kr = st[stage_slot<D, FP8>(0, 16 * h + n, 4 * u + gq)];
+      const u32x4 vr = st[stage_slot<D, FP8>(1, 16 * h + n, 4 * u + gq)];
+      if constexpr (FP8) {
+        kop[h][2 * u] = fp8x8_to_bf16(kr[0], kr[1]);
+        kop[h][2 * u + 1] = fp8x8_to_bf16(kr[2], kr[3]);
+        vop[h][2 * u] = fp8x8_to_bf16(vr[0], vr[1]);
+        vop[h][2 * u + 1] = fp8x8_to_bf16(vr[2], vr[3]);
+      } else {
+        kop[h][u] = kr;
+        vop[h][u] = vr;
+      }
     }
   }
 }
@@ -156,27 +218,13 @@ __device__ __forceinline__ void load_chunk(Chunk<D, FP8>& ch, const uint8_t* __r
 // Online-softmax update of one 32-token chunk. acc[blk] holds O^T for head-dim
 // block blk (lane: rows 4*gq+v of the block, column n); m in log2 units.
 template <int D, bool FP8>
-__device__ __forceinline__ void process_chunk(const Chunk<D, FP8>& ch, const u32x4 (&qf)[D / 32],
+__device__ __forceinline__ void process_chunk(u32x4 (&kop)[2][D / 32], u32x4 (&vop)[2][D / 32],
+                                              const u32x4 (&qf)[D / 32],
                                               const u32x4 (&sel)[2], f32x4 (&acc)[D / 16],
                                               float& m, float& lsum, float& lexact, int j0, int lim,
                                               int tile_end, float c_qk, float v_mul, int n,
                                               int gq) {
   using C = Cfg<D, FP8>;
-  u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
-      if constexpr (FP8) {
-        const u32x4 kr = ch.k[h][s >> 1], vr = ch.v[h][s >> 1];
-        kop[h][s] = (s & 1) ? fp8x8_to_bf16(kr[2], kr[3]) : fp8x8_to_bf16(kr[0], kr[1]);
-        vop[h][s] = (s & 1) ? fp8x8_to_bf16(vr[2], vr[3]) : fp8x8_to_bf16(vr[0], vr[1]);
-      } else {
-        kop[h][s] = ch.k[h][s];
-        vop[h][s] = ch.v[h][s];
-      }
-    }
-  }
   // Tokens at or past the tile end may be unwritten cache memory: zero their V so
   // that a zero probability cannot meet a NaN in P.V. Lane l loaded token l % 16.
   if (j0 + 32 > tile_end) {
@@ -263,8 +311,9 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     const int32_t* __restrict__ worker_offsets, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, const DecodeShape sh) {
   using C = Cfg<D, FP8>;
-  constexpr int kLdsStride = D + 4;
-  __shared__ float lds_o[kWaves][kMaxRows][kLdsStride];
+  // Each wave's region stages its chunks and, after its last chunk, holds its
+  // unnormalised output rows [16][D] for the merge.
+  __shared__ u32x4 lds_stage[kWaves][C::kStageVec];
   __shared__ float lds_m[kWaves][kMaxRows];
   __shared__ float lds_l[kWaves][kMaxRows];
   __shared__ float lds_le[kWaves][kMaxRows];
@@ -288,7 +337,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   const int M = sh.rows;
   const int Tq = sh.q_len;
   const int G = sh.group;
-  const int lane_off = n * C::kRowBytes + 16 * gq;
+  u32x4* const my_stage = lds_stage[wid];
   const int first = worker_offsets[blockIdx.x];
   const int last = worker_offsets[blockIdx.x + 1];
 
@@ -340,34 +389,31 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       }
     };
 
-    // Two register buffers alternate: while one chunk is computed the next one's
-    // loads are in flight, and the block-table offsets of the one after are read.
-    // Past the wave's last chunk the prefetch repeats the wave's own latest chunk
-    // (a cache hit), so every iteration issues the same loads.
-    int c0 = wid;
-    if (c0 < nchunks) {
-      Chunk<D, FP8> A, B;
-      HalfOffsets hoA = chunk_offsets(it, c0);
-      load_chunk<D, FP8>(A, k_cache, v_cache, hoA, lane_off);
-      int c1 = c0 + kWaves;
-      HalfOffsets hoB = c1 < nchunks ? chunk_offsets(it, c1) : hoA;
+    // One register buffer: a chunk's loads land in `raw`, are copied to the wave's
+    // LDS stage, and the next chunk's loads are issued into `raw` before the chunk
+    // is computed.
+    int c = wid;
+    if (c < nchunks) {
+      Raw<D, FP8> raw;
+      const HalfOffsets ho = chunk_offsets(it, c);
+      load_raw<D, FP8>(raw, k_cache, v_cache, ho, lane);
+      int cn = c + kWaves;
+      HalfOffsets hn = cn < nchunks ? chunk_offsets(it, cn) : ho;
       for (;;) {
-        load_chunk<D, FP8>(B, k_cache, v_cache, hoB, lane_off);
-        const int c2 = c1 + kWaves;
-        hoA = c2 < nchunks ? chunk_offsets(it, c2) : hoB;
-        chunk_scales(c0);
-        process_chunk<D, FP8>(A, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c0, lim, it.tile_end,
-                              c_qk, v_mul, n, gq);
-        if (c1 >= nchunks) break;
-        load_chunk<D, FP8>(A, k_cache, v_cache, hoA, lane_off);
-        const int c3 = c2 + kWaves;
-        hoB = c3 < nchunks ? chunk_offsets(it, c3) : hoA;
-        chunk_scales(c1);
-        process_chunk<D, FP8>(B, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c1, lim, it.tile_end,
-                              c_qk, v_mul, n, gq);
-        if (c2 >= nchunks) break;
-        c0 = c2;
-        c1 = c3;
+        stage_write<D, FP8>(my_stage, raw, lane);
+        if (cn < nchunks) load_raw<D, FP8>(raw, k_cache, v_cache, hn, lane);
+        chunk_scales(c);
+        u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
+        stage_read<D, FP8>(my_stage, kop, vop, n, gq);
+        process_chunk<D, FP8>(kop, vop, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c, lim,
+                              it.tile_end, c_qk, v_mul, n, gq);
+        if (cn >= nchunks) break;
+        // The scalar block-table reads for the chunk after next are waited for at the
+        // top of the next iteration, together with that chunk's data.
+        const int cnn = cn + kWaves;
+        if (cnn < nchunks) hn = chunk_offsets(it, cnn);
+        c = cn;
+        cn = cnn;
       }
     }
 
@@ -381,12 +427,13 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       lds_l[wid][n] = lsum;
       lds_le[wid][n] = lexact;
     }
+    float* const my_rows = reinterpret_cast<float*>(my_stage);   // [16][D]
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) lds_o[wid][n][out_dim<FP8>(s, c, gq, v)] = acc[2 * s + c][v];
+        for (int v = 0; v < 4; ++v) my_rows[n * D + out_dim<FP8>(s, c, gq, v)] = acc[2 * s + c][v];
     __syncthreads();
 
     // Merge the waves' partial softmax states and write the item's partial.
@@ -402,7 +449,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float f = __builtin_amdgcn_exp2f(lds_m[w][r] - mx);
-          num += f * lds_o[w][r][d];
+          num += f * reinterpret_cast<const float*>(lds_stage[w])[r * D + d];
           den += f * lds_l[w][r];
         }
         o = num / den;
