@@ -14,10 +14,18 @@ lengths differ. The pages give no cost, order or tie rule; the readings here:
   the lowest worker index; a worker's items are kept in assignment order;
 - partial slot of item (b, g, i): Hkv * req_tile_base[b] + g * n_b + i, where
   req_tile_base is the prefix sum of n_b;
-- automatic tile size (tile_tokens == 0): candidates quantum * 2**k <= 4096
-  (quantum = page size for bf16, lcm(page size, 64) for fp8); the estimate
-  makespan_tokens * 2 * D * eb + (max_items_per_worker + ceil(N / W)) * M * (D+1) * 4
-  is minimised, ties going to the larger tile.
+- automatic tile size (tile_tokens == 0), a bandwidth-sharing cost model:
+  candidates quantum * 2**k <= 65536 (quantum = page size for bf16,
+  lcm(page size, 64) for fp8); with kv(x) = x * 2 * D * eb bytes, the estimate
+      max(kv(sum of tokens), WORKER_RATIO * kv(makespan_tokens))
+      + max_items_per_worker * ITEM_BYTES + N * M * (D + 1) * 8
+  is minimised, ties going to the larger tile. On a memory-bound chip, workers that
+  finish early hand their bandwidth to the others, so imbalance costs nothing
+  until the busiest worker alone runs longer than the whole chip's stream:
+  WORKER_RATIO is how many times faster the chip streams than one worker, and
+  ITEM_BYTES the fixed cost of one work item expressed in chip-wide bytes (both
+  measured on MI355X: ~160x, ~2.6 us at ~6.5 TB/s). The last term is the partials
+  written and read back by the combine.
 
 This is the plain definition (a full sort and a heap over every item); the native
 planner uses an equivalent faster form and must match it bit for bit.
@@ -28,7 +36,9 @@ import math
 
 import numpy as np
 
-MAX_AUTO_TILE = 4096
+MAX_AUTO_TILE = 65536
+WORKER_RATIO = 160
+ITEM_BYTES = 1 << 24
 
 
 def num_tiles(L, T):
@@ -79,6 +89,7 @@ def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_
     quantum = tile_quantum(page_size, kv_format)
     eb = 2 if kv_format == "bf16" else 1
     M = (num_q_heads // num_kv_heads) * q_len
+    total = num_kv_heads * sum(int(L) for L in seq_lens)
     cands = []
     T = quantum
     while True:
@@ -92,7 +103,9 @@ def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_
         makespan = int(p["loads"].max())
         counts = np.diff(p["worker_offsets"]).astype(np.int64)
         N = int(counts.sum())
-        est = makespan * 2 * head_dim * eb + (int(counts.max()) + (N + W - 1) // W) * M * (head_dim + 1) * 4
+        kv = 2 * head_dim * eb
+        est = (max(total * kv, WORKER_RATIO * makespan * kv) + int(counts.max()) * ITEM_BYTES
+               + N * M * (head_dim + 1) * 8)
         if best_est is None or est < best_est or (est == best_est and T > best_T):
             best_T, best_est = T, est
     return best_T

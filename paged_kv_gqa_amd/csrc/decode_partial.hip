@@ -302,6 +302,35 @@ struct DecodeShape {
   float qk_scale_log2;
 };
 
+// Wave-uniform description of one work item.
+struct ItemInfo {
+  ItemCtx it;
+  int b, g, slot, L, nchunks;
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ ItemInfo item_info(const int32_t* __restrict__ items,
+                                              const int32_t* __restrict__ seq_lens,
+                                              const int32_t* __restrict__ block_table,
+                                              const DecodeShape& sh, int itx) {
+  using C = Cfg<D, FP8>;
+  ItemInfo r;
+  r.b = items[4 * itx + 0];
+  r.g = items[4 * itx + 1];
+  const int ti = items[4 * itx + 2];
+  r.slot = items[4 * itx + 3];
+  r.L = seq_lens[r.b];
+  r.it.bt = block_table + static_cast<int64_t>(r.b) * sh.bt_stride;
+  r.it.row_bytes = C::kRowBytes;
+  r.it.head_off = static_cast<int64_t>(r.g) * sh.page_size * C::kRowBytes;
+  r.it.page_bytes = static_cast<int64_t>(sh.num_kv_heads) * sh.page_size * C::kRowBytes;
+  r.it.tile_start = ti * sh.tile_tokens;
+  r.it.tile_end = min(r.L, r.it.tile_start + sh.tile_tokens);
+  r.it.page_size = sh.page_size;
+  r.nchunks = (r.it.tile_end - r.it.tile_start + 31) >> 5;
+  return r;
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_cache,
@@ -311,8 +340,8 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     const int32_t* __restrict__ worker_offsets, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, const DecodeShape sh) {
   using C = Cfg<D, FP8>;
-  // Each wave's region stages its chunks and, after its last chunk, holds its
-  // unnormalised output rows [16][D] for the merge.
+  // Each wave's region stages its chunks and, after its last chunk of an item,
+  // holds its unnormalised output rows [16][D] for the merge.
   __shared__ u32x4 lds_stage[kWaves][C::kStageVec];
   __shared__ float lds_m[kWaves][kMaxRows];
   __shared__ float lds_l[kWaves][kMaxRows];
@@ -321,8 +350,9 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
-  const int n = lane & 15;   // query row owned by this lane (and K/V row it loads)
+  const int n = lane & 15;   // query row owned by this lane (and K/V row it reads)
   const int gq = lane >> 4;  // 16-lane group
+  u32x4* const my_stage = lds_stage[wid];
 
   // Selection matrices: sel[c] has a 1 where operand k = 16c + n (bf16 1.0 = 0x3f80).
   u32x4 sel[2];
@@ -337,84 +367,85 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   const int M = sh.rows;
   const int Tq = sh.q_len;
   const int G = sh.group;
-  u32x4* const my_stage = lds_stage[wid];
   const int first = worker_offsets[blockIdx.x];
   const int last = worker_offsets[blockIdx.x + 1];
 
-  for (int itx = first; itx < last; ++itx) {
-    const int b = items[4 * itx + 0];
-    const int g = items[4 * itx + 1];
-    const int ti = items[4 * itx + 2];
-    const int slot = items[4 * itx + 3];
-    const int L = seq_lens[b];
-
-    ItemCtx it;
-    it.bt = block_table + static_cast<int64_t>(b) * sh.bt_stride;
-    it.row_bytes = C::kRowBytes;
-    it.head_off = static_cast<int64_t>(g) * sh.page_size * C::kRowBytes;
-    it.page_bytes = static_cast<int64_t>(sh.num_kv_heads) * sh.page_size * C::kRowBytes;
-    it.tile_start = ti * sh.tile_tokens;
-    it.tile_end = min(L, it.tile_start + sh.tile_tokens);
-    it.page_size = sh.page_size;
-
-    // Query fragment of row n (zero for padding rows n >= M) and its causal limit.
-    u32x4 qf[C::kSteps];
-    int lim = it.tile_end;
-    if (n < M) {
-      const int t = n / G;
-      const int head = g * G + (n - t * G);
-      const uint16_t* qrow = q + ((static_cast<int64_t>(b) * Tq + t) * sh.num_q_heads + head) * D;
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s)
-        qf[s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
-      lim = min(lim, L - Tq + t + 1);
-    } else {
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+  // The wave's work is a stream of units (item, chunk): chunks wid, wid + 4, ... of
+  // each of the worker's items. `raw` always holds the next unit's K/V in flight, and
+  // `qf_next` the query fragment of its item, so an item's first chunk is loaded
+  // while the previous item is still being computed and merged.
+  Raw<D, FP8> raw;
+  u32x4 qf_next[C::kSteps];
+  int u_itx = -1, u_c = 0;
+  ItemInfo u_info;
+  auto find_unit = [&](int from) {  // first unit of this wave in items >= from
+    u_itx = -1;
+    for (int x = from; x < last; ++x) {
+      const ItemInfo inf = item_info<D, FP8>(items, seq_lens, block_table, sh, x);
+      if (wid < inf.nchunks) {
+        u_itx = x;
+        u_c = wid;
+        u_info = inf;
+        return;
+      }
     }
+  };
+  auto issue_unit = [&]() {
+    if (u_itx < 0) return;
+    load_raw<D, FP8>(raw, k_cache, v_cache, chunk_offsets(u_info.it, u_c), lane);
+    if (u_c == wid) {  // first chunk of an item: fetch that item's query fragment
+      if (n < M) {
+        const int t = n / G;
+        const int head = u_info.g * G + (n - t * G);
+        const uint16_t* qrow =
+            q + ((static_cast<int64_t>(u_info.b) * Tq + t) * sh.num_q_heads + head) * D;
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s)
+          qf_next[s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
+      } else {
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) qf_next[s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  find_unit(first);
+  issue_unit();
+
+  for (int itx = first; itx < last; ++itx) {
+    const ItemInfo cur = (u_itx == itx) ? u_info
+                                        : item_info<D, FP8>(items, seq_lens, block_table, sh, itx);
+    // Causal limit of row n (draft token t sees keys up to L - Tq + t); padding rows
+    // n >= M see the whole tile.
+    int lim = cur.it.tile_end;
+    if (n < M) lim = min(lim, cur.L - Tq + n / G + 1);
+    u32x4 qf[C::kSteps];
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) qf[s] = qf_next[s];
 
     f32x4 acc[C::kBlocks];
 #pragma unroll
     for (int bl = 0; bl < C::kBlocks; ++bl) acc[bl] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f, lexact = 0.f;
 
-    const int nchunks = (it.tile_end - it.tile_start + 31) >> 5;
-    float c_qk = sh.qk_scale_log2, v_mul = 1.f;
-    auto chunk_scales = [&](int chunk) {
+    while (u_itx == itx) {
+      const int c = u_c;
+      stage_write<D, FP8>(my_stage, raw, lane);
+      if (c + kWaves < cur.nchunks)
+        u_c = c + kWaves;
+      else
+        find_unit(itx + 1);
+      issue_unit();
+      float c_qk = sh.qk_scale_log2, v_mul = 1.f;
       if constexpr (FP8) {
-        const int j0 = it.tile_start + 32 * chunk;
-        const int64_t sidx = static_cast<int64_t>(it.bt[j0 / it.page_size]) * sh.num_kv_heads + g;
+        const int j0 = cur.it.tile_start + 32 * c;
+        const int64_t sidx = static_cast<int64_t>(cur.it.bt[j0 / cur.it.page_size]) * sh.num_kv_heads + cur.g;
         c_qk = sh.qk_scale_log2 * k_scale[sidx];
         v_mul = v_scale[sidx];
       }
-    };
-
-    // One register buffer: a chunk's loads land in `raw`, are copied to the wave's
-    // LDS stage, and the next chunk's loads are issued into `raw` before the chunk
-    // is computed.
-    int c = wid;
-    if (c < nchunks) {
-      Raw<D, FP8> raw;
-      const HalfOffsets ho = chunk_offsets(it, c);
-      load_raw<D, FP8>(raw, k_cache, v_cache, ho, lane);
-      int cn = c + kWaves;
-      HalfOffsets hn = cn < nchunks ? chunk_offsets(it, cn) : ho;
-      for (;;) {
-        stage_write<D, FP8>(my_stage, raw, lane);
-        if (cn < nchunks) load_raw<D, FP8>(raw, k_cache, v_cache, hn, lane);
-        chunk_scales(c);
-        u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
-        stage_read<D, FP8>(my_stage, kop, vop, n, gq);
-        process_chunk<D, FP8>(kop, vop, qf, sel, acc, m, lsum, lexact, it.tile_start + 32 * c, lim,
-                              it.tile_end, c_qk, v_mul, n, gq);
-        if (cn >= nchunks) break;
-        // The scalar block-table reads for the chunk after next are waited for at the
-        // top of the next iteration, together with that chunk's data.
-        const int cnn = cn + kWaves;
-        if (cnn < nchunks) hn = chunk_offsets(it, cnn);
-        c = cn;
-        cn = cnn;
-      }
+      u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
+      stage_read<D, FP8>(my_stage, kop, vop, n, gq);
+      process_chunk<D, FP8>(kop, vop, qf, sel, acc, m, lsum, lexact, cur.it.tile_start + 32 * c, lim,
+                            cur.it.tile_end, c_qk, v_mul, n, gq);
     }
 
     // Wave result -> LDS: row max, full row sums, unnormalised O.
@@ -437,7 +468,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     __syncthreads();
 
     // Merge the waves' partial softmax states and write the item's partial.
-    float* wo = ws_o + static_cast<int64_t>(slot) * M * D;
+    float* wo = ws_o + static_cast<int64_t>(cur.slot) * M * D;
     for (int e = tid; e < M * D; e += kThreads) {
       const int r = e / D, d = e - r * D;
       float mx = lds_m[0][r];
@@ -467,7 +498,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
         for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][tid] - mx) * lds_le[w][tid];
         lse = (mx + __builtin_amdgcn_logf(den)) * kLn2;
       }
-      ws_lse[static_cast<int64_t>(slot) * M + tid] = lse;
+      ws_lse[static_cast<int64_t>(cur.slot) * M + tid] = lse;
     }
     __syncthreads();
   }

@@ -16,7 +16,13 @@ namespace pkv {
 
 namespace {
 
-constexpr int64_t kMaxAutoTile = 4096;
+constexpr int64_t kMaxAutoTile = 65536;
+// Automatic tile size, a bandwidth-sharing cost model (measured on MI355X): the chip
+// streams ~kWorkerRatio times faster than one worker, so load imbalance only costs
+// once the busiest worker alone outlasts the whole chip's stream; each work item
+// has a fixed cost of ~kItemBytes of chip-wide streaming (~2.6 us at ~6.5 TB/s).
+constexpr int64_t kWorkerRatio = 160;
+constexpr int64_t kItemBytes = int64_t{1} << 24;
 
 // Tournament tree over the workers' loads. A key packs (load, worker) into one
 // 64-bit word, load in the high bits, so the smaller key is the less-loaded worker
@@ -133,9 +139,9 @@ PlanStats plan_stats(int batch, const int32_t* seq_lens, int Hkv, int64_t T, int
 int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_q_heads,
                          int Hkv, int head_dim, int page_size, bool fp8, int W) {
   const int64_t quantum = tile_quantum(page_size, fp8);
-  const int64_t eb = fp8 ? 1 : 2;
+  const int64_t kv = 2 * static_cast<int64_t>(head_dim) * (fp8 ? 1 : 2);  // bytes per token
   const int64_t M = static_cast<int64_t>(num_q_heads / Hkv) * q_len;
-  const int64_t item_cost = M * (head_dim + 1) * 4;
+  const int64_t partial_bytes = M * (head_dim + 1) * 8;  // written, then read by combine
   int64_t total = 0;
   for (int b = 0; b < batch; ++b) total += seq_lens[b];
   total *= Hkv;
@@ -144,18 +150,15 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
     cands.push_back(T);
     if (T * 2 > kMaxAutoTile) break;
   }
-  // Largest tile first, so a tie keeps the larger tile by strict improvement only.
-  // A candidate whose lower bound (perfect balance, ceil(N/W) items per worker) is
-  // not below the best estimate cannot win and is not simulated.
   // Candidates are quantum * 2^k, so floor(L / T) = floor(L / quantum) >> k.
   Scratch s;
-  std::vector<int32_t> lq(batch), lr(batch);
-  for (int b = 0; b < batch; ++b) {
-    lq[b] = static_cast<int32_t>(seq_lens[b] / quantum);
-    lr[b] = seq_lens[b] - static_cast<int32_t>(lq[b] * quantum);
-  }
+  std::vector<int32_t> lq(batch);
+  for (int b = 0; b < batch; ++b) lq[b] = static_cast<int32_t>(seq_lens[b] / quantum);
   s.nfull.resize(batch);
   s.rem.resize(batch);
+  // Largest tile first, so a tie keeps the larger tile by strict improvement only.
+  // A candidate whose lower bound (the exact full-tile phase, perfect balance) is
+  // not below the best estimate cannot win and is not simulated.
   int64_t best_T = cands.back(), best_est = -1;
   for (int k = static_cast<int>(cands.size()) - 1; k >= 0; --k) {
     const int64_t T = cands[k];
@@ -168,16 +171,15 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
       partial += (s.rem[b] != 0);
     }
     const int64_t n_items = (f + partial) * Hkv;
-    const int64_t per_worker = ceil_div(n_items, W);
-    // Lower bounds: the loads and item counts after the exact full-tile phase only
-    // grow, and no plan beats perfect balance.
     const int64_t full_per_worker = ceil_div(f * Hkv, W);
     const int64_t span_lb = std::max(ceil_div(total, W), full_per_worker * T);
-    const int64_t lower = span_lb * 2 * head_dim * eb +
-                          (std::max(per_worker, full_per_worker) + per_worker) * item_cost;
+    const int64_t items_lb = std::max(ceil_div(n_items, W), full_per_worker);
+    const int64_t tail = n_items * partial_bytes;
+    const int64_t lower = std::max(total * kv, kWorkerRatio * span_lb * kv) + items_lb * kItemBytes + tail;
     if (best_est >= 0 && lower >= best_est) continue;  // cannot improve strictly
     const PlanStats st = plan_stats_impl(batch, Hkv, T, W, f, s);
-    const int64_t est = st.makespan * 2 * head_dim * eb + (st.max_items + per_worker) * item_cost;
+    const int64_t est = std::max(total * kv, kWorkerRatio * st.makespan * kv) +
+                        st.max_items * kItemBytes + tail;
     if (best_est < 0 || est < best_est) {
       best_T = T;
       best_est = est;

@@ -91,20 +91,25 @@ def test_graham_lpt_bound(seq_lens, W):
 
 
 def test_auto_tile_hand_worked():
-    # one request of 64 tokens, D=64, bf16, M=1, W=4: T=16 gives makespan 16 and
-    # one item per worker: 16*2*64*2 + (1+1)*1*65*4 = 4616; T=32: 8192 + 520;
-    # T>=64: 16384 + 520. So T=16.
+    # kv bytes per token = 2*D*eb = 256 (D=64, bf16); item bytes 2^24; partials M*(D+1)*8 = 520.
+    # One request of 64 tokens on 4 workers: T=16 -> 4 items, makespan 16:
+    # 160*16*256 + 2^24 + 4*520 = 17434656; T=32 -> 160*32*256 + 2^24 + 2*520 = 18088976;
+    # T>=64 -> 160*64*256 + 2^24 + 520 = 19399176. So T=16.
     assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4) == 16
-    # W=1: T=16 -> 16384 + (4+4)*260; T=32 -> 16384 + (2+2)*260; T>=64 -> 16384 + 2*260
-    # for every T from 64 to 4096 (a tie), so the largest candidate wins.
-    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 1) == 4096
+    # One worker: T=16 puts 4 items on it (4*2^24); every T >= 64 gives one item and the
+    # same estimate, a tie that goes to the largest candidate.
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 1) == P.MAX_AUTO_TILE
+    # One request of 65536 tokens on 64 workers: total/W = 1024 tokens, so the makespan
+    # term 160*makespan*256 is minimal (and above the total) at one 1024-token tile per
+    # worker; smaller tiles add a second item per worker, larger ones double the makespan.
+    assert P.auto_tile_tokens([65536], 1, 1, 1, 64, 16, "bf16", 64) == 1024
     # fp8 with page 16: the quantum is lcm(16, 64) = 64
     assert P.tile_quantum(16, "fp8") == 64 and P.tile_quantum(64, "fp8") == 64
     assert P.tile_quantum(32, "bf16") == 32
 
 
-@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 4096, 512), ("mixed", 2048, 4256),
-                                      ("long", 2048, 512), ("fp8_spec", 512, 4712)])
+@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 65536, 512), ("mixed", 65536, 1024),
+                                      ("long", 4096, 256), ("fp8_spec", 8192, 424)])
 def test_auto_tile_on_workloads(name, T, N):
     import synth
     cfg = synth.ALL[name]
