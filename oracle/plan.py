@@ -16,16 +16,18 @@ lengths differ. The pages give no cost, order or tie rule; the readings here:
   req_tile_base is the prefix sum of n_b;
 - automatic tile size (tile_tokens == 0), a bandwidth-sharing cost model:
   candidates quantum * 2**k <= 65536 (quantum = page size for bf16,
-  lcm(page size, 64) for fp8); with kv(x) = x * 2 * D * eb bytes, the estimate
-      max(kv(sum of tokens), WORKER_RATIO * kv(makespan_tokens))
-      + max_items_per_worker * ITEM_BYTES + N * M * (D + 1) * 8
-  is minimised, ties going to the larger tile. On a memory-bound chip, workers that
-  finish early hand their bandwidth to the others, so imbalance costs nothing
-  until the busiest worker alone runs longer than the whole chip's stream:
-  WORKER_RATIO is how many times faster the chip streams than one worker, and
-  ITEM_BYTES the fixed cost of one work item expressed in chip-wide bytes (both
-  measured on MI355X: ~160x, ~2.6 us at ~6.5 TB/s). The last term is the partials
-  written and read back by the combine.
+  lcm(page size, 64) for fp8); the estimate
+      kv * fluid(worker loads) + max_items_per_worker * ITEM_BYTES + N * M * (D + 1) * 8
+  (kv = 2 * D * eb bytes per token) is minimised, ties going to the larger tile.
+  fluid() is the streaming time of the plan on a memory-bound chip, in chip-byte
+  units: while k workers are busy each streams at min(chip / k, chip / WORKER_RATIO),
+  so with the loads sorted ascending, l_1 <= ... <= l_W (l_0 = 0),
+      fluid = sum_j (l_j - l_(j-1)) * max(W - j + 1, WORKER_RATIO).
+  It equals the total when enough workers stay busy to the end and grows with the
+  tail the busiest workers leave. WORKER_RATIO (how many workers saturate the chip)
+  and ITEM_BYTES (the fixed cost of one work item in chip-wide bytes, ~2.6 us at
+  ~6.5 TB/s) were measured on MI355X. The last term is the partials written and read
+  back by the combine.
 
 This is the plain definition (a full sort and a heap over every item); the native
 planner uses an equivalent faster form and must match it bit for bit.
@@ -39,6 +41,17 @@ import numpy as np
 MAX_AUTO_TILE = 65536
 WORKER_RATIO = 160
 ITEM_BYTES = 1 << 24
+
+
+def fluid_cost(loads):
+    """Streaming time of per-worker token loads in chip-token units (see above)."""
+    l = sorted(int(x) for x in loads)
+    W = len(l)
+    total, prev = 0, 0
+    for j, x in enumerate(l):
+        total += (x - prev) * max(W - j, WORKER_RATIO)
+        prev = x
+    return total
 
 
 def num_tiles(L, T):
@@ -89,7 +102,6 @@ def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_
     quantum = tile_quantum(page_size, kv_format)
     eb = 2 if kv_format == "bf16" else 1
     M = (num_q_heads // num_kv_heads) * q_len
-    total = num_kv_heads * sum(int(L) for L in seq_lens)
     cands = []
     T = quantum
     while True:
@@ -100,12 +112,10 @@ def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_
     best_T, best_est = None, None
     for T in cands:
         p = lpt_plan(seq_lens, num_kv_heads, T, W)
-        makespan = int(p["loads"].max())
         counts = np.diff(p["worker_offsets"]).astype(np.int64)
         N = int(counts.sum())
         kv = 2 * head_dim * eb
-        est = (max(total * kv, WORKER_RATIO * makespan * kv) + int(counts.max()) * ITEM_BYTES
-               + N * M * (head_dim + 1) * 8)
+        est = kv * fluid_cost(p["loads"]) + int(counts.max()) * ITEM_BYTES + N * M * (head_dim + 1) * 8
         if best_est is None or est < best_est or (est == best_est and T > best_T):
             best_T, best_est = T, est
     return best_T

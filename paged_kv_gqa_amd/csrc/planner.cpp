@@ -17,10 +17,11 @@ namespace pkv {
 namespace {
 
 constexpr int64_t kMaxAutoTile = 65536;
-// Automatic tile size, a bandwidth-sharing cost model (measured on MI355X): the chip
-// streams ~kWorkerRatio times faster than one worker, so load imbalance only costs
-// once the busiest worker alone outlasts the whole chip's stream; each work item
-// has a fixed cost of ~kItemBytes of chip-wide streaming (~2.6 us at ~6.5 TB/s).
+// Automatic tile size, a bandwidth-sharing cost model (measured on MI355X): while k
+// workers are busy each streams at min(chip / k, chip / kWorkerRatio), so the plan's
+// streaming time in chip-token units is sum_j (l_j - l_(j-1)) * max(W - j + 1,
+// kWorkerRatio) over the loads sorted ascending; each work item adds a fixed cost
+// of ~kItemBytes of chip-wide streaming (~2.6 us at ~6.5 TB/s).
 constexpr int64_t kWorkerRatio = 160;
 constexpr int64_t kItemBytes = int64_t{1} << 24;
 
@@ -40,24 +41,33 @@ class WorkerTree {
     for (int w = 0; w < W; ++w)
       node_[size_ + w] = (static_cast<uint64_t>(loads[w]) << kWorkerBits) | static_cast<uint64_t>(w);
     for (int i = size_ - 1; i >= 1; --i) node_[i] = std::min(node_[2 * i], node_[2 * i + 1]);
+    root_ = node_[1];
   }
-  // Add `cost` to the least-loaded worker (lowest index on ties); returns it.
+  // Add `cost` to the least-loaded worker (lowest index on ties); returns it. The
+  // new minimum is carried up in a register (the siblings' keys are the only
+  // loads), and the root stays cached for the next call.
   int32_t place(int64_t cost) {
-    const uint64_t top = node_[1];
-    const int32_t w = static_cast<int32_t>(top & ((uint64_t{1} << kWorkerBits) - 1));
+    const int32_t w = static_cast<int32_t>(root_ & ((uint64_t{1} << kWorkerBits) - 1));
     int i = size_ + w;
-    node_[i] = top + (static_cast<uint64_t>(cost) << kWorkerBits);
-    for (i >>= 1; i >= 1; i >>= 1) node_[i] = std::min(node_[2 * i], node_[2 * i + 1]);
+    uint64_t v = root_ + (static_cast<uint64_t>(cost) << kWorkerBits);
+    node_[i] = v;
+    while (i > 1) {
+      v = std::min(v, node_[i ^ 1]);
+      i >>= 1;
+      node_[i] = v;
+    }
+    root_ = v;
     return w;
   }
 
  private:
   int size_ = 1;
+  uint64_t root_ = UINT64_MAX;
   std::vector<uint64_t> node_;
 };
 
 struct Scratch {
-  std::vector<int64_t> loads, counts, full;
+  std::vector<int64_t> loads, counts, full, sorted;
   std::vector<int32_t> reqs, nfull, rem;  // per request: full tiles, last-tile tokens
   WorkerTree heap;
 };
@@ -84,6 +94,29 @@ void partial_requests(int batch, Scratch& s) {
   const int32_t* rem = s.rem.data();
   std::stable_sort(s.reqs.begin(), s.reqs.end(),
                    [rem](int32_t x, int32_t y) { return rem[x] > rem[y]; });
+}
+
+// Streaming time of the per-worker loads in chip-token units (see kWorkerRatio):
+// sum_j (l_j - l_(j-1)) * max(W - j + 1, R) over the loads sorted ascending. The
+// weights exceed the busy-worker count only for the R - 1 largest loads, so this is
+// the total plus sum (l_j - l_(j-1)) * (R - (W - j + 1)) over those positions; only
+// the top R loads need sorting.
+__int128 fluid_cost(std::vector<int64_t>& v, const std::vector<int64_t>& loads) {
+  const int64_t W = static_cast<int64_t>(loads.size());
+  const int64_t R = kWorkerRatio;
+  int64_t total = 0, top = 0;
+  for (int64_t x : loads) {
+    total += x;
+    top = std::max(top, x);
+  }
+  if (W <= R) return static_cast<__int128>(R) * top;  // every weight is R
+  v.assign(loads.begin(), loads.end());
+  std::nth_element(v.begin(), v.begin() + (W - R), v.end());
+  std::sort(v.begin() + (W - R), v.end());
+  __int128 extra = 0;
+  for (int64_t i = W - R + 1; i < W; ++i)  // 0-based i has W - i busy workers
+    extra += static_cast<__int128>(v[i] - v[i - 1]) * (R - (W - i));
+  return total + extra;
 }
 
 // Full-tile phase: loads and counts after round-robin placement.
@@ -142,8 +175,11 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
   const int64_t kv = 2 * static_cast<int64_t>(head_dim) * (fp8 ? 1 : 2);  // bytes per token
   const int64_t M = static_cast<int64_t>(num_q_heads / Hkv) * q_len;
   const int64_t partial_bytes = M * (head_dim + 1) * 8;  // written, then read by combine
-  int64_t total = 0;
-  for (int b = 0; b < batch; ++b) total += seq_lens[b];
+  int64_t total = 0, max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    total += seq_lens[b];
+    max_len = std::max<int64_t>(max_len, seq_lens[b]);
+  }
   total *= Hkv;
   std::vector<int64_t> cands;
   for (int64_t T = quantum;; T *= 2) {
@@ -156,31 +192,54 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
   for (int b = 0; b < batch; ++b) lq[b] = static_cast<int32_t>(seq_lens[b] / quantum);
   s.nfull.resize(batch);
   s.rem.resize(batch);
-  // Largest tile first, so a tie keeps the larger tile by strict improvement only.
-  // A candidate whose lower bound (the exact full-tile phase, perfect balance) is
-  // not below the best estimate cannot win and is not simulated.
-  int64_t best_T = cands.back(), best_est = -1;
-  for (int k = static_cast<int>(cands.size()) - 1; k >= 0; --k) {
+  // Lower bound of every candidate first (O(B) each): fluid >= total (every phase
+  // weighs at least its worker count) and fluid >= kWorkerRatio * makespan (every
+  // phase weighs at least kWorkerRatio); the loads and item counts of the exact
+  // full-tile phase only grow. Candidates are then simulated in increasing order of
+  // their bound, and one whose bound cannot beat (or tie with a larger tile) the best
+  // estimate so far is skipped. Ties go to the larger tile, independent of order.
+  const int K = static_cast<int>(cands.size());
+  std::vector<__int128> lower(K);
+  std::vector<int64_t> fulls(K);
+  for (int k = 0; k < K; ++k) {
     const int64_t T = cands[k];
     int64_t f = 0, partial = 0;
     for (int b = 0; b < batch; ++b) {
       const int32_t q = lq[b] >> k;
-      s.nfull[b] = q;
-      s.rem[b] = seq_lens[b] - static_cast<int32_t>(q * T);
       f += q;
-      partial += (s.rem[b] != 0);
+      partial += (seq_lens[b] != static_cast<int32_t>(q * T));
     }
+    fulls[k] = f;
     const int64_t n_items = (f + partial) * Hkv;
     const int64_t full_per_worker = ceil_div(f * Hkv, W);
-    const int64_t span_lb = std::max(ceil_div(total, W), full_per_worker * T);
+    // The makespan is also at least the largest single item, min(max L, T).
+    const int64_t span_lb =
+        std::max({ceil_div(total, W), full_per_worker * T, std::min<int64_t>(max_len, T)});
     const int64_t items_lb = std::max(ceil_div(n_items, W), full_per_worker);
-    const int64_t tail = n_items * partial_bytes;
-    const int64_t lower = std::max(total * kv, kWorkerRatio * span_lb * kv) + items_lb * kItemBytes + tail;
-    if (best_est >= 0 && lower >= best_est) continue;  // cannot improve strictly
-    const PlanStats st = plan_stats_impl(batch, Hkv, T, W, f, s);
-    const int64_t est = std::max(total * kv, kWorkerRatio * st.makespan * kv) +
-                        st.max_items * kItemBytes + tail;
-    if (best_est < 0 || est < best_est) {
+    lower[k] = static_cast<__int128>(kv) * std::max(total, kWorkerRatio * span_lb) +
+               static_cast<__int128>(items_lb) * kItemBytes +
+               static_cast<__int128>(n_items) * partial_bytes;
+  }
+  std::vector<int> order(K);
+  for (int k = 0; k < K; ++k) order[k] = k;
+  std::sort(order.begin(), order.end(), [&](int a, int b) {
+    return lower[a] < lower[b] || (lower[a] == lower[b] && a > b);
+  });
+  int64_t best_T = -1;
+  __int128 best_est = -1;
+  for (int k : order) {
+    const int64_t T = cands[k];
+    if (best_T >= 0 && (lower[k] > best_est || (lower[k] == best_est && T < best_T))) continue;
+    for (int b = 0; b < batch; ++b) {
+      const int32_t q = lq[b] >> k;
+      s.nfull[b] = q;
+      s.rem[b] = seq_lens[b] - static_cast<int32_t>(q * T);
+    }
+    const PlanStats st = plan_stats_impl(batch, Hkv, T, W, fulls[k], s);
+    const __int128 est = static_cast<__int128>(kv) * fluid_cost(s.sorted, s.loads) +
+                         static_cast<__int128>(st.max_items) * kItemBytes +
+                         static_cast<__int128>(st.num_items) * partial_bytes;
+    if (best_T < 0 || est < best_est || (est == best_est && T > best_T)) {
       best_T = T;
       best_est = est;
     }

@@ -90,6 +90,18 @@ def test_graham_lpt_bound(seq_lens, W):
     assert 3 * W * int(p["loads"].max()) <= (4 * W - 1) * opt
 
 
+def test_fluid_cost_hand_worked():
+    # equal loads: one phase of W busy workers -> weight max(W, 160)
+    assert P.fluid_cost([5, 5, 5]) == 5 * 160
+    assert P.fluid_cost([7] * 200) == 7 * 200
+    # 161 workers with 1 token and one with 11 (W = 162): the first token streams with
+    # 162 busy workers (1 * 162), the last 10 tokens of the busiest worker alone at the
+    # single-worker rate (10 * 160).
+    assert P.fluid_cost([1] * 161 + [11]) == 162 + 1600
+    # W <= 160: every phase weighs 160, so the cost is 160 * the largest load
+    assert P.fluid_cost([3, 9, 1]) == 160 * 9
+
+
 def test_auto_tile_hand_worked():
     # kv bytes per token = 2*D*eb = 256 (D=64, bf16); item bytes 2^24; partials M*(D+1)*8 = 520.
     # One request of 64 tokens on 4 workers: T=16 -> 4 items, makespan 16:
@@ -108,7 +120,7 @@ def test_auto_tile_hand_worked():
     assert P.tile_quantum(32, "bf16") == 32
 
 
-@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 65536, 512), ("mixed", 65536, 1024),
+@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 65536, 512), ("mixed", 16384, 1224),
                                       ("long", 4096, 256), ("fp8_spec", 8192, 424)])
 def test_auto_tile_on_workloads(name, T, N):
     import synth
