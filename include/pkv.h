@@ -121,7 +121,9 @@ int pkv_default_num_workers(int device, int kv_format, int head_dim, int* out);
 int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim,
                         size_t* out);
 
-/* Arguments of pkv_decode_partial. Device pointers unless noted. */
+/* Arguments of pkv_decode_partial. Pointers are device-accessible: device memory,
+ * or (for the small plan arrays and seq_lens) mapped pinned host memory, which the
+ * kernels then read directly without a host-to-device copy. */
 typedef struct pkv_decode_args {
   size_t struct_size;             /* sizeof(pkv_decode_args) */
   const void* q;                  /* bf16 [B, Tq, Hq, D] */
@@ -131,7 +133,7 @@ typedef struct pkv_decode_args {
   const float* v_scale;           /* fp32 [num_pages, Hkv]; NULL iff bf16 */
   const int32_t* block_table;     /* int32 [B, bt_stride] */
   const int32_t* seq_lens;        /* int32 [B]; must equal the plan's seq_lens_h */
-  const int32_t* items;           /* int32 [num_items][4] from pkv_plan */
+  const int32_t* items;           /* int32 [num_items][4] from pkv_plan (16-byte aligned) */
   const int32_t* worker_offsets;  /* int32 [num_workers + 1] from pkv_plan */
   const int32_t* req_tile_base;   /* int32 [B + 1] from pkv_plan */
   void* workspace;                /* pkv_workspace_bytes(num_partials, M, D) bytes */

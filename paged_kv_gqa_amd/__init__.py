@@ -227,21 +227,55 @@ def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batc
 # Per-step runner
 
 
-class PagedDecode:
-    """One decode step = host plan + one H2D copy of the plan + decode_partial + combine,
-    enqueued on the current torch stream with no host synchronisation.
+_HIP_HOST_MALLOC_MAPPED = 0x2
+_HIP_HOST_MALLOC_COHERENT = 0x40000000
 
-    With ``side_stream_upload`` the plan copy runs on a side stream, so it overlaps
-    the previous step's kernels, and the current stream waits for it (an event)
-    before decode_partial; otherwise it is enqueued on the current stream. Plans go
-    through rings of pinned and device buffers: a pinned buffer is rewritten only
-    after the copy that read it has completed, a device buffer only after the
-    kernels that read it have completed. Buffers grow on demand and are kept, so at
-    a fixed shape no allocation happens after the first steps."""
+
+class HostPlanBuffer:
+    """Pinned, device-mapped, coherent host memory for one step's plan.
+
+    The kernels read the plan straight from here (zero-copy), so the step needs no
+    host-to-device copy. Coherent memory is not cached by the GPU, so every launch
+    sees what the host wrote before it."""
+
+    _hip = None
+
+    def __init__(self, nbytes):
+        if HostPlanBuffer._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
+            hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+            hip.hipHostMalloc.restype = ctypes.c_int
+            hip.hipHostFree.argtypes = [ctypes.c_void_p]
+            hip.hipHostFree.restype = ctypes.c_int
+            HostPlanBuffer._hip = hip
+        self._ptr = ctypes.c_void_p()
+        rc = HostPlanBuffer._hip.hipHostMalloc(ctypes.byref(self._ptr), nbytes,
+                                               _HIP_HOST_MALLOC_MAPPED | _HIP_HOST_MALLOC_COHERENT)
+        if rc != 0 or not self._ptr.value:
+            raise RuntimeError("hipHostMalloc(%d bytes, coherent) failed: %d" % (nbytes, rc))
+        self.nbytes = nbytes
+        self.addr = self._ptr.value
+        self.array = np.ctypeslib.as_array((ctypes.c_int32 * (nbytes // 4)).from_address(self.addr))
+
+    def free(self):
+        hip = type(self)._hip
+        if hip is not None and self._ptr is not None and self._ptr.value:
+            hip.hipHostFree(self._ptr)
+        self._ptr = None
+
+
+class PagedDecode:
+    """One decode step = host plan + decode_partial + combine, enqueued on the current
+    torch stream with no host synchronisation.
+
+    The plan is written into a ring of coherent pinned buffers that the kernels read
+    directly (no host-to-device copy on the step's critical path). A buffer is
+    rewritten only after the kernels of the step that last read it have completed
+    (an event per buffer). The workspace grows on demand and is kept, so at a fixed
+    shape no allocation happens after the first steps."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
-                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3,
-                 side_stream_upload=False):
+                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3):
         import torch
         self.torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
@@ -250,18 +284,30 @@ class PagedDecode:
         self.q_len, self.tile_tokens = q_len, tile_tokens
         self.rows = (num_q_heads // num_kv_heads) * q_len
         self.num_workers = num_workers or pkv_default_num_workers(self.device.index, kv_format, head_dim)
-        self._pinned = [None] * slots
-        self._dev = [None] * slots
-        self._copied = [None] * slots      # event on the copy stream: copy out of slot done
+        self._bufs = [None] * slots
         self._consumed = [None] * slots    # event on the compute stream: kernels reading slot done
         self._slot = 0
-        self._copy_stream = torch.cuda.Stream(device=self.device) if side_stream_upload else None
         self._workspace = None
         self.last_plan = None
 
+    def close(self):
+        """Free the plan buffers (after the kernels that read them have completed)."""
+        for k, buf in enumerate(getattr(self, "_bufs", [])):
+            if buf is not None:
+                ev = self._consumed[k]
+                if ev is not None:
+                    ev.synchronize()
+                buf.free()
+                self._bufs[k] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001  (interpreter shutdown: the process releases it)
+            pass
+
     def plan(self, seq_lens_h):
-        """Host plan into the next pinned buffer; returns a dict describing it."""
-        torch = self.torch
+        """Host plan into the next plan buffer; returns a dict describing it."""
         sl = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
         T, N, NP = pkv_plan_query(sl, self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim,
                                   self.page_size, self.kv_format, self.tile_tokens, self.num_workers)
@@ -271,43 +317,24 @@ class PagedDecode:
         n_sl = n_rtb + _round4(B + 1)
         total = n_sl + _round4(B)
         k = self._slot
-        self._slot = (k + 1) % len(self._pinned)
-        if self._copied[k] is not None:
-            self._copied[k].synchronize()          # the copy that last read this buffer is done
-        buf = self._pinned[k]
-        if buf is None or buf.numel() < total:
-            buf = torch.empty(max(total, 1024), dtype=torch.int32, pin_memory=True)
-            self._pinned[k] = buf
-        h = buf.numpy()
+        self._slot = (k + 1) % len(self._bufs)
+        if self._consumed[k] is not None:
+            self._consumed[k].synchronize()        # the kernels that last read this buffer are done
+        buf = self._bufs[k]
+        if buf is None or buf.nbytes < 4 * total:
+            if buf is not None:
+                buf.free()
+            buf = HostPlanBuffer(4 * max(total, 1024))
+            self._bufs[k] = buf
+        h = buf.array
         pkv_plan(sl, self.q_len, self.num_kv_heads, T, W,
                  out=(h[:n_off].reshape(N, 4), h[n_off:n_off + W + 1], h[n_rtb:n_rtb + B + 1]))
         h[n_sl:n_sl + B] = sl
-        p = dict(T=T, N=N, NP=NP, W=W, B=B, total=total, n_off=n_off, n_rtb=n_rtb, n_sl=n_sl, slot=k)
+        a = buf.addr
+        p = dict(T=T, N=N, NP=NP, W=W, B=B, slot=k, items=a, worker_offsets=a + 4 * n_off,
+                 req_tile_base=a + 4 * n_rtb, seq_lens=a + 4 * n_sl)
         self.last_plan = p
         return p
-
-    def upload(self, p):
-        """Copy the plan on the side stream; make the current stream wait for it."""
-        torch = self.torch
-        k, total = p["slot"], p["total"]
-        main = torch.cuda.current_stream(self.device)
-        dev = self._dev[k]
-        if dev is None or dev.numel() < total:
-            torch.cuda.synchronize(self.device)    # rare: no kernel may still read the old buffer
-            dev = torch.empty(max(total, 1024), dtype=torch.int32, device=self.device)
-            self._dev[k] = dev
-        cs = self._copy_stream or main
-        if self._copy_stream is not None and self._consumed[k] is not None:
-            cs.wait_event(self._consumed[k])
-        with torch.cuda.stream(cs):
-            dev[:total].copy_(self._pinned[k][:total], non_blocking=True)
-            if self._copied[k] is None:
-                self._copied[k] = torch.cuda.Event()
-            self._copied[k].record(cs)
-        if self._copy_stream is not None:
-            main.wait_event(self._copied[k])
-        return (dev[:p["n_off"]], dev[p["n_off"]:p["n_rtb"]], dev[p["n_rtb"]:p["n_sl"]],
-                dev[p["n_sl"]:p["n_sl"] + p["B"]])
 
     def workspace(self, num_partials):
         nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)
@@ -320,8 +347,8 @@ class PagedDecode:
                  v_scale=None, seq_lens=None, out=None, lse_out=None, stream=None,
                  partial_events=None):
         """Run one decode step. ``seq_lens_h`` (host ints) drives the plan; ``seq_lens``
-        (device int32) defaults to a copy uploaded with the plan. ``partial_events``: two
-        torch.cuda.Events recorded around the decode_partial launch (for timing)."""
+        (device int32) defaults to the copy written next to the plan. ``partial_events``:
+        two torch.cuda.Events recorded around the decode_partial launch (for timing)."""
         if stream is not None:
             with self.torch.cuda.stream(stream):
                 return self(q, k_cache, v_cache, block_table, seq_lens_h, scale, k_scale=k_scale,
@@ -329,9 +356,8 @@ class PagedDecode:
                             partial_events=partial_events)
         torch = self.torch
         p = self.plan(seq_lens_h)
-        items, offs, rtb, sl_dev = self.upload(p)
         if seq_lens is None:
-            seq_lens = sl_dev
+            seq_lens = p["seq_lens"]
         ws, ws_bytes = self.workspace(p["NP"])
         B = p["B"]
         if out is None:
@@ -340,9 +366,9 @@ class PagedDecode:
         if partial_events is not None:
             partial_events[0].record()
         pkv_decode_partial(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-                           seq_lens=seq_lens, items=items, worker_offsets=offs, req_tile_base=rtb,
-                           workspace=ws, workspace_bytes=ws_bytes, num_items=p["N"],
-                           num_partials=p["NP"], num_pages=k_cache.shape[0], batch=B,
+                           seq_lens=seq_lens, items=p["items"], worker_offsets=p["worker_offsets"],
+                           req_tile_base=p["req_tile_base"], workspace=ws, workspace_bytes=ws_bytes,
+                           num_items=p["N"], num_partials=p["NP"], num_pages=k_cache.shape[0], batch=B,
                            q_len=self.q_len, num_q_heads=self.num_q_heads,
                            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
                            page_size=self.page_size, bt_stride=block_table.shape[1],
@@ -350,9 +376,10 @@ class PagedDecode:
                            scale=scale, k_scale=k_scale, v_scale=v_scale)
         if partial_events is not None:
             partial_events[1].record()
-        pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"], req_tile_base=rtb,
-                    batch=B, q_len=self.q_len, num_q_heads=self.num_q_heads,
-                    num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, out=out, lse_out=lse_out)
+        pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
+                    req_tile_base=p["req_tile_base"], batch=B, q_len=self.q_len,
+                    num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
+                    head_dim=self.head_dim, out=out, lse_out=lse_out)
         k = p["slot"]
         if self._consumed[k] is None:
             self._consumed[k] = torch.cuda.Event()
