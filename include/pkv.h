@@ -11,7 +11,9 @@
  *
  * One decode step through this ABI:
  *   1. pkv_plan_query + pkv_plan   (host; builds the work list from seq_lens)
- *   2. copy items / worker_offsets / req_tile_base to the device (caller)
+ *   2. make items / worker_offsets / req_tile_base device-accessible (caller):
+ *      copy them to device memory, or write them into mapped coherent pinned
+ *      host memory that the kernels read directly
  *   3. pkv_decode_partial          (enqueued on a HIP stream)
  *   4. pkv_combine                 (enqueued on the same stream)
  *
@@ -79,9 +81,13 @@ const char* pkv_last_error(void);
  *
  * seq_lens_h : host int32 [batch]. tile_tokens: T, a multiple of the quantum
  * (P for bf16, lcm(P, 64) for fp8), or 0 for the automatic choice: among
- * quantum * 2^k <= 4096 the T minimising
- *   makespan_tokens(T) * 2 * D * eb + (max_items_per_worker(T) + ceil(N(T) / W)) * M * (D + 1) * 4
- * (eb = bytes per KV element), ties going to the larger T. num_workers: W >= 1
+ * quantum * 2^k <= 65536 the T minimising the bandwidth-sharing estimate
+ *   kv * fluid(loads) + max_items_per_worker * 2^24 + N * M * (D + 1) * 8,
+ * kv = 2 * D * eb bytes per token (eb = bytes per KV element), where with the
+ * per-worker token loads sorted ascending l_1 <= ... <= l_W (l_0 = 0)
+ *   fluid = sum_j (l_j - l_(j-1)) * max(W - j + 1, 160)
+ * (while k workers are busy each streams at min(chip/k, chip/160)); ties go to the
+ * larger T. num_workers: W >= 1
  * (see pkv_default_num_workers). Outputs: the resolved T, N = number of work
  * items, and the number of partial slots (= N).
  * Errors: INVALID_ARG (null pointer, batch < 0, W < 1), UNSUPPORTED (shape
