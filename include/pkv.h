@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 1
 
 /* KV element formats. FP8 is OCP e4m3fn (bias 7, max 448, no infinities). */
 enum pkv_kv_format { PKV_KV_BF16 = 0, PKV_KV_FP8_E4M3FN = 1 };
@@ -122,12 +122,8 @@ int pkv_plan(int batch, const int32_t* seq_lens_h, int q_len, int num_kv_heads,
 int pkv_default_num_workers(int device, int kv_format, int head_dim, int* out);
 
 /* Workspace bytes for num_partials partial results of rows_per_partial (= M) rows
- * of D fp32 values plus one fp32 log-sum-exp per row, and num_partials int32
- * completion counters; layout: o block at offset 0, lse block at the next 256-byte
- * boundary, counters at the next 256-byte boundary after that. The counters are used
- * only by the fused combine of pkv_decode_partial: they must be zero before the first
- * such call and every completed call leaves them zero (zero the workspace once when
- * it is allocated). Errors: INVALID_ARG. */
+ * of D fp32 values plus one fp32 log-sum-exp per row; layout: o block at offset
+ * 0, lse block at the next 256-byte boundary. Errors: INVALID_ARG. */
 int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim,
                         size_t* out);
 
@@ -156,14 +152,6 @@ typedef struct pkv_decode_args {
   int tile_tokens;                /* resolved T of the plan */
   int num_workers;                /* W of the plan */
   float scale;                    /* softmax scale applied to q.k (e.g. 1/sqrt(D)) */
-  /* ABI version 2: optional fused combine. When `out` is set, the workgroup that
-   * completes the last tile of a (request, kv head) merges that group's partials
-   * (same rule as pkv_combine, in tile order) and writes `out` / `lse_out`; no
-   * pkv_combine call is needed. The workspace counters must be zero before the first
-   * such call (see pkv_workspace_bytes). Callers built for version 1 pass a
-   * struct_size that ends before these fields and get the unfused behaviour. */
-  void* out;                      /* bf16 [B, Tq, Hq, D] or NULL */
-  float* lse_out;                 /* fp32 [B, Tq, Hq] or NULL; ignored without out */
 } pkv_decode_args;
 
 /*
@@ -173,7 +161,6 @@ typedef struct pkv_decode_args {
  * r = t*G + j (query token t, head g*G + j), the normalised partial output o
  * (fp32 [D]) and its log-sum-exp (fp32, natural log; -inf with o = 0 when the
  * causal mask hides every key of the tile from that row) into slot `slot`.
- * With args->out set it also performs the combine (see pkv_decode_args).
  * `stream` is a hipStream_t (NULL = null stream). Enqueue only; no sync.
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (q, caches, workspace must be
  * 16-byte aligned), WORKSPACE, HIP (launch failure).

@@ -61,7 +61,6 @@ class DecodeArgs(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
         ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("tile_tokens", ctypes.c_int),
         ("num_workers", ctypes.c_int), ("scale", ctypes.c_float),
-        ("out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p),
     ]
 
 
@@ -199,9 +198,8 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
                        req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
                        batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
                        kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
-                       out=None, lse_out=None, stream=None):
-    """Enqueue the split-KV partial kernel (with ``out``: and the fused combine).
-    Device arguments are tensors or raw addresses."""
+                       stream=None):
+    """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
     a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
@@ -214,7 +212,6 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
     a.head_dim, a.page_size, a.bt_stride = head_dim, page_size, bt_stride
     a.kv_format = KV_FORMATS.get(kv_format, kv_format)
     a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
-    a.out, a.lse_out = _ptr(out), _ptr(lse_out)
     _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
 
 
@@ -275,14 +272,10 @@ class PagedDecode:
     directly (no host-to-device copy on the step's critical path). A buffer is
     rewritten only after the kernels of the step that last read it have completed
     (an event per buffer). The workspace grows on demand and is kept, so at a fixed
-    shape no allocation happens after the first steps.
-
-    With ``fused_combine`` the decode kernel also merges each (request, kv head)'s
-    partials as soon as its last tile completes, and no combine kernel is launched."""
+    shape no allocation happens after the first steps."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
-                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3,
-                 fused_combine=False):
+                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3):
         import torch
         self.torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
@@ -291,7 +284,6 @@ class PagedDecode:
         self.q_len, self.tile_tokens = q_len, tile_tokens
         self.rows = (num_q_heads // num_kv_heads) * q_len
         self.num_workers = num_workers or pkv_default_num_workers(self.device.index, kv_format, head_dim)
-        self.fused_combine = fused_combine
         self._bufs = [None] * slots
         self._consumed = [None] * slots    # event on the compute stream: kernels reading slot done
         self._slot = 0
@@ -348,8 +340,7 @@ class PagedDecode:
         nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)
         if self._workspace is None or self._workspace.numel() < nbytes:
             self.torch.cuda.synchronize(self.device)
-            # zeroed once: the fused combine's counters start at zero and stay zero
-            self._workspace = self.torch.zeros(nbytes, dtype=self.torch.uint8, device=self.device)
+            self._workspace = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
         return self._workspace, nbytes
 
     def __call__(self, q, k_cache, v_cache, block_table, seq_lens_h, scale, *, k_scale=None,
@@ -382,16 +373,13 @@ class PagedDecode:
                            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
                            page_size=self.page_size, bt_stride=block_table.shape[1],
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
-                           scale=scale, k_scale=k_scale, v_scale=v_scale,
-                           out=out if self.fused_combine else None,
-                           lse_out=lse_out if self.fused_combine else None)
+                           scale=scale, k_scale=k_scale, v_scale=v_scale)
         if partial_events is not None:
             partial_events[1].record()
-        if not self.fused_combine:
-            pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
-                        req_tile_base=p["req_tile_base"], batch=B, q_len=self.q_len,
-                        num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
-                        head_dim=self.head_dim, out=out, lse_out=lse_out)
+        pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
+                    req_tile_base=p["req_tile_base"], batch=B, q_len=self.q_len,
+                    num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
+                    head_dim=self.head_dim, out=out, lse_out=lse_out)
         k = p["slot"]
         if self._consumed[k] is None:
             self._consumed[k] = torch.cuda.Event()

@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
-#include <cstddef>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -164,20 +163,15 @@ int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim
                 static_cast<long long>(num_partials), rows_per_partial, head_dim);
   const size_t o = static_cast<size_t>(num_partials) * rows_per_partial * head_dim * 4;
   const size_t l = static_cast<size_t>(num_partials) * rows_per_partial * 4;
-  const size_t c = static_cast<size_t>(num_partials) * 4;
-  *out = align256(o) + align256(l) + align256(c);
+  *out = align256(o) + align256(l);
   return PKV_OK;
 }
 
 int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   if (a == nullptr) return fail(PKV_ERR_INVALID_ARG, "null args");
-  // Version-1 callers end the struct before the fused-combine fields.
-  const size_t v1_size = offsetof(pkv_decode_args, out);
-  if (a->struct_size < v1_size)
-    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size, v1_size);
-  const bool has_v2 = a->struct_size >= sizeof(pkv_decode_args);
-  void* const fused_out = has_v2 ? a->out : nullptr;
-  float* const fused_lse = has_v2 && fused_out ? a->lse_out : nullptr;
+  if (a->struct_size < sizeof(pkv_decode_args))
+    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size,
+                sizeof(pkv_decode_args));
   int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
                        a->kv_format);
   if (st != PKV_OK) return st;
@@ -201,10 +195,8 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   if (fp8 != (a->k_scale != nullptr) || fp8 != (a->v_scale != nullptr))
     return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale must be given exactly for fp8 KV");
   if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
-      !aligned(a->workspace, 16) || (fused_out && !aligned(fused_out, 16)) ||
-      (fused_lse && !aligned(fused_lse, 4)))
-    return fail(PKV_ERR_ALIGNMENT,
-                "q, k_cache, v_cache, workspace and out must be 16-byte aligned");
+      !aligned(a->workspace, 16))
+    return fail(PKV_ERR_ALIGNMENT, "q, k_cache, v_cache and workspace must be 16-byte aligned");
   if (!aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) || !aligned(a->items, 16) ||
       !aligned(a->worker_offsets, 4) || (fp8 && (!aligned(a->k_scale, 4) || !aligned(a->v_scale, 4))))
     return fail(PKV_ERR_ALIGNMENT, "int32/fp32 arrays misaligned (items need 16 bytes)");
@@ -226,13 +218,9 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   p.items = a->items;
   p.worker_offsets = a->worker_offsets;
   p.ws_o = static_cast<float*>(a->workspace);
-  const size_t o_bytes = align256(static_cast<size_t>(a->num_partials) * rows * a->head_dim * 4);
-  const size_t l_bytes = align256(static_cast<size_t>(a->num_partials) * rows * 4);
-  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + o_bytes);
-  p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(a->workspace) + o_bytes + l_bytes);
-  p.req_tile_base = a->req_tile_base;
-  p.out = static_cast<uint16_t*>(fused_out);
-  p.lse_out = fused_lse;
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) +
+                                      align256(static_cast<size_t>(a->num_partials) * rows *
+                                               a->head_dim * 4));
   p.q_len = a->q_len;
   p.num_q_heads = a->num_q_heads;
   p.num_kv_heads = a->num_kv_heads;

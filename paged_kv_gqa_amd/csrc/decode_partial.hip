@@ -49,7 +49,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kLog2e = 1.44269504088896341f;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -339,9 +338,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
     const int32_t* __restrict__ worker_offsets, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int32_t* __restrict__ counters,
-    const int32_t* __restrict__ req_tile_base, uint16_t* __restrict__ out,
-    float* __restrict__ lse_out, const DecodeShape sh) {
+    float* __restrict__ ws_lse, const DecodeShape sh) {
   using C = Cfg<D, FP8>;
   // Each wave's region stages its chunks and, after its last chunk of an item,
   // holds its unnormalised output rows [16][D] for the merge.
@@ -349,7 +346,6 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   __shared__ float lds_m[kWaves][kMaxRows];
   __shared__ float lds_l[kWaves][kMaxRows];
   __shared__ float lds_le[kWaves][kMaxRows];
-  __shared__ int lds_last;
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -504,42 +500,6 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       }
       ws_lse[static_cast<int64_t>(cur.slot) * M + tid] = lse;
     }
-
-    // Fused combine: the workgroup that completes the last tile of this (request,
-    // kv head) merges its partials. Every thread publishes its stores device-wide
-    // before one thread counts the tile; the last one acquires, merges in tile order
-    // and resets the counter for the next call.
-    if (out != nullptr) {
-      __threadfence();
-      __syncthreads();
-      const int nb = (cur.L + sh.tile_tokens - 1) / sh.tile_tokens;
-      int32_t* const cnt = counters + static_cast<int64_t>(cur.b) * sh.num_kv_heads + cur.g;
-      if (tid == 0) lds_last = (atomicAdd(cnt, 1) == nb - 1);
-      __syncthreads();
-      if (lds_last) {
-        __threadfence();
-        const int64_t slot0 = static_cast<int64_t>(sh.num_kv_heads) * req_tile_base[cur.b] +
-                              static_cast<int64_t>(cur.g) * nb;
-        for (int e = tid; e < M * D; e += kThreads) {
-          const int r = e / D, d = e - r * D;
-          float mx = -INFINITY;
-          for (int i = 0; i < nb; ++i) mx = fmaxf(mx, ws_lse[(slot0 + i) * M + r]);
-          const float m_use = (mx == -INFINITY) ? 0.f : mx * kLog2e;
-          float num = 0.f, den = 0.f;
-          for (int i = 0; i < nb; ++i) {
-            const float w = __builtin_amdgcn_exp2f(ws_lse[(slot0 + i) * M + r] * kLog2e - m_use);
-            num += w * ws_o[((slot0 + i) * M + r) * D + d];
-            den += w;
-          }
-          const int t = r / G, h = cur.g * G + (r - t * G);
-          const int64_t orow = (static_cast<int64_t>(cur.b) * Tq + t) * sh.num_q_heads + h;
-          out[orow * D + d] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(den > 0.f ? num / den : 0.f));
-          if (d == 0 && lse_out != nullptr)
-            lse_out[orow] = den > 0.f ? (m_use + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
-        }
-        if (tid == 0) *cnt = 0;
-      }
-    }
     __syncthreads();
   }
 }
@@ -554,8 +514,7 @@ hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8, 
 #define PKV_LAUNCH(DIM, F8)                                                                   \
   hipLaunchKernelGGL((decode_partial_kernel<DIM, F8>), grid, block, 0, stream, p.q, p.k_cache, \
                      p.v_cache, p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items,     \
-                     p.worker_offsets, p.ws_o, p.ws_lse, p.counters, p.req_tile_base, p.out,    \
-                     p.lse_out, sh)
+                     p.worker_offsets, p.ws_o, p.ws_lse, sh)
   if (head_dim == 128) {
     if (fp8)
       PKV_LAUNCH(128, true);

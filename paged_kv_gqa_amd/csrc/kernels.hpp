@@ -26,10 +26,6 @@ struct DecodeParams {
   const int32_t* worker_offsets;
   float* ws_o;                // [num_partials, M, D]
   float* ws_lse;              // [num_partials, M]
-  int32_t* counters;          // [num_partials] completion counters (fused combine)
-  const int32_t* req_tile_base;  // [B + 1]
-  uint16_t* out;              // bf16 [B, Tq, Hq, D] for the fused combine, or null
-  float* lse_out;             // [B, Tq, Hq] or null
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
   float qk_scale_log2;        // softmax scale * log2(e)
 };

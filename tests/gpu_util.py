@@ -29,19 +29,18 @@ def device_inputs(inp):
     return dict(q=q, k=k, v=v, ks=ks, vs=vs, bt=bt, sl=sl)
 
 
-def make_runner(inp, tile_tokens=0, num_workers=0, fused=False):
+def make_runner(inp, tile_tokens=0, num_workers=0):
     import paged_kv_gqa_amd as pkv
     return pkv.PagedDecode(num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
                            head_dim=inp.head_dim, page_size=inp.page_size, kv_format=inp.kv_format,
-                           q_len=inp.q_len, tile_tokens=tile_tokens, num_workers=num_workers,
-                           fused_combine=fused)
+                           q_len=inp.q_len, tile_tokens=tile_tokens, num_workers=num_workers)
 
 
-def run_decode(inp, tile_tokens=0, num_workers=0, dev=None, runner=None, fused=False):
+def run_decode(inp, tile_tokens=0, num_workers=0, dev=None, runner=None):
     """Returns (out float32 numpy [B,Tq,Hq,D], lse float32 numpy [B,Tq,Hq], out bf16 bits)."""
     import torch
     dev = dev or device_inputs(inp)
-    runner = runner or make_runner(inp, tile_tokens, num_workers, fused)
+    runner = runner or make_runner(inp, tile_tokens, num_workers)
     B = inp.batch
     lse = torch.empty((B, inp.q_len, inp.num_q_heads), dtype=torch.float32, device="cuda")
     out = runner(dev["q"], dev["k"], dev["v"], dev["bt"], inp.seq_lens, inp.scale,

@@ -272,30 +272,6 @@ def test_combine_alone_matches_lse_merge():
                 assert abs(got_lse[b, t, h] - ref_l) <= 1e-5 * max(1.0, abs(ref_l))
 
 
-FUSED = [c for c in SMALL if c["id"] in ("tiny_T16_W1", "g4_d128_p16", "g4_d128_p16_T48", "g16_d128",
-                                         "spec4_g4", "spec2_g8_d64", "fp8_spec4", "fp8_d64", "fp8_auto_g8")]
-
-
-@pytest.mark.parametrize("case", FUSED, ids=[c["id"] for c in FUSED])
-def test_fused_combine_matches_oracle(case):
-    """decode_partial with the fused combine (the last workgroup of each request and kv
-    head merges its partials) against the oracle, twice in a row on one runner: the
-    completion counters must come back to zero after every call."""
-    inp = synth.make_inputs(dict(case["c"]), seed=23, poison=True, slack_pages=3, seq_lens=case.get("sl"))
-    dev = device_inputs(inp)
-    runner = make_runner(inp, case["T"], case["W"], fused=True)
-    out1, lse1, b1 = run_decode(inp, dev=dev, runner=runner)
-    check(inp, out1, lse1, tag=case["id"] + " fused")
-    out2, lse2, b2 = run_decode(inp, dev=dev, runner=runner)
-    assert np.array_equal(b1, b2) and np.array_equal(lse1, lse2)
-
-
-def test_fused_combine_many_splits():
-    inp = medium_inputs("bf16", q_len=2)
-    out, lse, _ = run_decode(inp, tile_tokens=16, num_workers=97, fused=True)
-    check(inp, out, lse, tag="fused T=16")
-
-
 def test_empty_batch_is_a_no_op():
     import torch
     inp = synth.make_inputs(cfg(), seed=0, seq_lens=[5])
