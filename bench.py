@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload mixed] [--gpus 1]
 
 One step = the whole hot path over one decode batch: host plan (uniform tiles,
-greedy bin-packing), one H2D copy of the plan, the split-KV partial kernel and the
-log-sum-exp combine kernel, all on one stream. Inputs (seeded, synthetic) are
+greedy bin-packing) written into mapped pinned memory that the kernels read in
+place, the split-KV partial kernel and the log-sum-exp combine kernel, all on one
+stream. Inputs (seeded, synthetic) are
 resident in HBM before timing starts. Prints ONE JSON line on stdout; progress
 goes to stderr.
 
@@ -183,7 +184,7 @@ def main():
             "work_items": plan["N"],
             "num_workers": plan["W"],
             "algorithmic_bytes_per_step": algo,
-            "step": "host plan + plan H2D + decode_partial + combine",
+            "step": "host plan (read in place by the kernels) + decode_partial + combine",
         },
         "roofline": {
             "kernel": "decode_partial",
