@@ -112,15 +112,19 @@ def _i32(a):
     return a, a.ctypes.data_as(_i32p)
 
 
-def _ptr(t):
-    """Address of a torch tensor / numpy array / int / None."""
+def _ptr(t, name="argument"):
+    """Device address of a device-side argument: a CUDA tensor, an int address (device
+    memory or mapped pinned host memory) or None. Anything else - a numpy array or a
+    CPU tensor lives in pageable host memory the GPU cannot read - raises TypeError
+    before the library sees it."""
     if t is None:
         return None
-    if isinstance(t, int):
-        return t
-    if hasattr(t, "data_ptr"):
+    if isinstance(t, (int, np.integer)) and not isinstance(t, bool):
+        return int(t)
+    if hasattr(t, "data_ptr") and getattr(t, "is_cuda", False):
         return t.data_ptr()
-    return t.ctypes.data
+    raise TypeError("%s must be a CUDA tensor, a device-accessible address or None, not %s"
+                    % (name, type(t).__name__ if not hasattr(t, "device") else "a tensor on %s" % t.device))
 
 
 def _stream_handle(stream):
@@ -202,11 +206,13 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
     """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
-    a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
-    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
-    a.block_table, a.seq_lens = _ptr(block_table), _ptr(seq_lens)
-    a.items, a.worker_offsets, a.req_tile_base = _ptr(items), _ptr(worker_offsets), _ptr(req_tile_base)
-    a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    a.q, a.k_cache, a.v_cache = _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
+    a.k_scale, a.v_scale = _ptr(k_scale, "k_scale"), _ptr(v_scale, "v_scale")
+    a.block_table, a.seq_lens = _ptr(block_table, "block_table"), _ptr(seq_lens, "seq_lens")
+    a.items = _ptr(items, "items")
+    a.worker_offsets = _ptr(worker_offsets, "worker_offsets")
+    a.req_tile_base = _ptr(req_tile_base, "req_tile_base")
+    a.workspace, a.workspace_bytes = _ptr(workspace, "workspace"), workspace_bytes
     a.num_items, a.num_partials, a.num_pages = num_items, num_partials, num_pages
     a.batch, a.q_len, a.num_q_heads, a.num_kv_heads = batch, q_len, num_q_heads, num_kv_heads
     a.head_dim, a.page_size, a.bt_stride = head_dim, page_size, bt_stride
@@ -218,9 +224,10 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
 def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batch, q_len,
                 num_q_heads, num_kv_heads, head_dim, out, lse_out=None, stream=None):
     """Enqueue the log-sum-exp combine kernel."""
-    _check(_lib.pkv_combine(_ptr(workspace), workspace_bytes, num_partials, _ptr(req_tile_base),
-                            batch, q_len, num_q_heads, num_kv_heads, head_dim, _ptr(out),
-                            _ptr(lse_out), _stream_handle(stream)), "pkv_combine")
+    _check(_lib.pkv_combine(_ptr(workspace, "workspace"), workspace_bytes, num_partials,
+                            _ptr(req_tile_base, "req_tile_base"), batch, q_len, num_q_heads,
+                            num_kv_heads, head_dim, _ptr(out, "out"), _ptr(lse_out, "lse_out"),
+                            _stream_handle(stream)), "pkv_combine")
 
 
 # ---------------------------------------------------------------------------------

@@ -182,6 +182,21 @@ def test_decode_partial_without_items_is_a_no_op():
     pkv.pkv_decode_partial(**decode_kwargs(num_items=0, num_partials=0))
 
 
+@pytest.mark.parametrize("name", ["q", "k_cache", "k_scale", "block_table", "seq_lens", "items",
+                                  "workspace"])
+def test_host_arrays_are_not_device_arguments(name):
+    """A numpy array or CPU tensor holds pageable host memory the kernels cannot read;
+    the binding refuses it before anything reaches the library."""
+    import torch
+    for host in (np.zeros(64, np.float32), torch.zeros(64)):
+        with pytest.raises(TypeError, match=name):
+            pkv.pkv_decode_partial(**decode_kwargs(**{name: host}))
+    with pytest.raises(TypeError, match="out"):
+        pkv.pkv_combine(workspace=9 * A, workspace_bytes=1 << 30, num_partials=4, req_tile_base=8 * A,
+                        batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        out=np.zeros(8, np.uint16), stream=0)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(out=A + 2), pkv.PKV_ERR_ALIGNMENT),
     (dict(workspace_bytes=16), pkv.PKV_ERR_WORKSPACE),
