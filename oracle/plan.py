@@ -97,8 +97,10 @@ def lpt_plan(seq_lens, num_kv_heads, T, W):
 
 
 def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_size,
-                     kv_format, W):
-    """The automatic tile size (see module docstring)."""
+                     kv_format, W, max_items=None):
+    """The automatic tile size (see module docstring). With ``max_items`` (the item
+    capacity of a plan built on the device) candidates whose plan has more items are
+    skipped; ValueError if none is left."""
     quantum = tile_quantum(page_size, kv_format)
     eb = 2 if kv_format == "bf16" else 1
     M = (num_q_heads // num_kv_heads) * q_len
@@ -114,16 +116,20 @@ def auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_
         p = lpt_plan(seq_lens, num_kv_heads, T, W)
         counts = np.diff(p["worker_offsets"]).astype(np.int64)
         N = int(counts.sum())
+        if max_items is not None and N > max_items:
+            continue
         kv = 2 * head_dim * eb
         est = kv * fluid_cost(p["loads"]) + int(counts.max()) * ITEM_BYTES + N * M * (head_dim + 1) * 8
         if best_est is None or est < best_est or (est == best_est and T > best_T):
             best_T, best_est = T, est
+    if best_T is None:
+        raise ValueError("no candidate tile has at most %d items" % max_items)
     return best_T
 
 
 def plan(seq_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_size, kv_format,
-         tile_tokens, W):
+         tile_tokens, W, max_items=None):
     """Resolve the tile size (0 = automatic) and build the plan."""
     T = tile_tokens or auto_tile_tokens(seq_lens, q_len, num_q_heads, num_kv_heads,
-                                        head_dim, page_size, kv_format, W)
+                                        head_dim, page_size, kv_format, W, max_items)
     return lpt_plan(seq_lens, num_kv_heads, T, W)

@@ -115,6 +115,14 @@ def test_auto_tile_hand_worked():
     # term 160*makespan*256 is minimal (and above the total) at one 1024-token tile per
     # worker; smaller tiles add a second item per worker, larger ones double the makespan.
     assert P.auto_tile_tokens([65536], 1, 1, 1, 64, 16, "bf16", 64) == 1024
+    # An item capacity skips the candidates with more items: with at most 3 items T=16
+    # (4 items) is out and T=32 (2 items, 18088976) beats T>=64 (19399176); with at most
+    # 1 item only T>=64 is left, the tie going to the largest; with 0 none is left.
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4, max_items=4) == 16
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4, max_items=3) == 32
+    assert P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4, max_items=1) == P.MAX_AUTO_TILE
+    with pytest.raises(ValueError):
+        P.auto_tile_tokens([64], 1, 1, 1, 64, 16, "bf16", 4, max_items=0)
     # fp8 with page 16: the quantum is lcm(16, 64) = 64
     assert P.tile_quantum(16, "fp8") == 64 and P.tile_quantum(64, "fp8") == 64
     assert P.tile_quantum(32, "bf16") == 32
