@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-plan", action="store_true",
+                    help="build the plan on the GPU (pkv_plan_device) from device seq_lens "
+                         "instead of on the host")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM counters)")
@@ -124,7 +127,8 @@ def main():
     runner = pkv.PagedDecode(num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
                              head_dim=inp.head_dim, page_size=inp.page_size,
                              kv_format=inp.kv_format, q_len=inp.q_len,
-                             tile_tokens=args.tile_tokens, num_workers=args.num_workers)
+                             tile_tokens=args.tile_tokens, num_workers=args.num_workers,
+                             device_plan=args.device_plan)
     out = torch.empty((inp.batch, inp.q_len, inp.num_q_heads, inp.head_dim), dtype=torch.bfloat16,
                       device=dev)
 
@@ -136,7 +140,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    plan = runner.last_plan
+    if args.device_plan:
+        info = runner.plan_info()
+        if info["status"] != 0:
+            raise RuntimeError("device plan failed: %s" % info)
+        plan = dict(T=info["T"], N=info["N"], W=runner.num_workers)
+        step_desc = "device plan (pkv_plan_device) + decode_partial + combine"
+    else:
+        plan = runner.last_plan
+        step_desc = "host plan (read in place by the kernels) + decode_partial + combine"
     log("plan: tile %d tokens, %d items, %d workers" % (plan["T"], plan["N"], plan["W"]))
 
     K = args.steps
@@ -184,7 +196,7 @@ def main():
             "work_items": plan["N"],
             "num_workers": plan["W"],
             "algorithmic_bytes_per_step": algo,
-            "step": "host plan (read in place by the kernels) + decode_partial + combine",
+            "step": step_desc,
         },
         "roofline": {
             "kernel": "decode_partial",

@@ -16,6 +16,10 @@
  *      host memory that the kernels read directly
  *   3. pkv_decode_partial          (enqueued on a HIP stream)
  *   4. pkv_combine                 (enqueued on the same stream)
+ * or, with no host work per step (e.g. inside a captured HIP graph):
+ *   1. pkv_plan_device             (enqueued; same work list, built on the GPU from
+ *                                   device seq_lens)
+ *   2. pkv_decode_partial + pkv_combine as above, sized by the plan's capacity
  *
  * Conventions
  * - Every buffer, host or device, is allocated and owned by the caller. The
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* KV element formats. FP8 is OCP e4m3fn (bias 7, max 448, no infinities). */
 enum pkv_kv_format { PKV_KV_BF16 = 0, PKV_KV_FP8_E4M3FN = 1 };
@@ -152,6 +156,10 @@ typedef struct pkv_decode_args {
   int tile_tokens;                /* resolved T of the plan */
   int num_workers;                /* W of the plan */
   float scale;                    /* softmax scale applied to q.k (e.g. 1/sqrt(D)) */
+  /* ABI 2. Device int32 holding T; when non-NULL it replaces tile_tokens (which is
+   * then not checked): pass info + 1 of pkv_plan_device. A struct_size that ends
+   * before this field (an ABI 1 caller) means NULL. */
+  const int32_t* tile_tokens_dev;
 } pkv_decode_args;
 
 /*
@@ -166,6 +174,52 @@ typedef struct pkv_decode_args {
  * 16-byte aligned), WORKSPACE, HIP (launch failure).
  */
 int pkv_decode_partial(const pkv_decode_args* args, void* stream);
+
+/* Bytes of scratch pkv_plan_device needs for these arguments (the same values as
+ * the pkv_plan_device call). With a fixed tile: 256 + 8 * batch * num_kv_heads.
+ * With the automatic tile every candidate tile's plan is built at once, so it
+ * holds, per candidate, its remainder-tile placements and a whole plan of up to
+ * max_items items. Errors: INVALID_ARG. */
+int pkv_plan_device_scratch_bytes(int batch, int num_kv_heads, int page_size, int kv_format,
+                                  int tile_tokens, int num_workers, int64_t max_items,
+                                  size_t* out);
+
+/*
+ * Device-side planner: the work list of pkv_plan_query + pkv_plan - the same
+ * uniform tiles, longest-first greedy placement onto the workers and slot order,
+ * bit for bit - built on the GPU from device seq_lens and enqueued on `stream`, so
+ * a decode step needs no host work and can be captured in a HIP graph and replayed
+ * with new lengths. The HPC-Ops review (section "How the kernels are organized
+ * around specific workload shapes") has the tiles assigned before every decode
+ * step; this entry point does that assignment on the device.
+ *
+ * tile_tokens: T (a multiple of the quantum) or 0 for the automatic rule of
+ * pkv_plan_query, evaluated on the device and restricted to the candidate tiles
+ * whose item count N fits max_items (the host's choice whenever that tile fits).
+ * Arguments (device memory unless noted; caller-owned):
+ *   seq_lens        int32 [batch]
+ *   items           int32 [max_items][4], 16-byte aligned; rows (b, g, i, slot)
+ *   worker_offsets  int32 [num_workers + 1]
+ *   req_tile_base   int32 [batch + 1]
+ *   info            int32 [4] = {status, T, N, most items on one worker}
+ *   scratch         pkv_plan_device_scratch_bytes(...) bytes, 16-byte aligned;
+ *                   contents need no initialisation
+ * Limits: 1 <= num_workers <= 1024, batch <= 4096, 0 <= max_items <= INT32_MAX / 4.
+ * Returned errors (nothing enqueued): INVALID_ARG, UNSUPPORTED (shape rules, the
+ * limits, tile not a multiple of the quantum), ALIGNMENT, WORKSPACE (scratch too
+ * small), HIP. Errors found on the device go to info[0] with an empty plan (every
+ * worker_offsets and req_tile_base entry 0: decode_partial then does nothing and
+ * combine writes zeros with lse -inf): SEQ (some L_b < max(1, q_len)), UNSUPPORTED
+ * (num_kv_heads * sum of L_b >= 2^36), WORKSPACE (N > max_items).
+ * Then call pkv_decode_partial with num_items = num_partials = max_items,
+ * tile_tokens_dev = info + 1 and a workspace for max_items partials, and
+ * pkv_combine with num_partials = max_items.
+ */
+int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_heads,
+                    int num_kv_heads, int head_dim, int page_size, int kv_format,
+                    int tile_tokens, int num_workers, int64_t max_items, int32_t* items,
+                    int32_t* worker_offsets, int32_t* req_tile_base, int32_t* info,
+                    void* scratch, size_t scratch_bytes, void* stream);
 
 /*
  * Log-sum-exp merge of the partials of each row (b, t, h):

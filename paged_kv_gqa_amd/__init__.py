@@ -2,8 +2,9 @@
 
 Thin ctypes wrappers with the C ABI's names (argument marshalling only; every step
 of the decode path runs in the library), plus ``PagedDecode``, a per-step runner
-that plans on the host, uploads the plan on the caller's stream and enqueues the
-two kernels. PyTorch supplies device memory and streams.
+that plans on the host into mapped pinned memory the kernels read in place (or, with
+``device_plan=True``, enqueues the device-side planner) and enqueues the two kernels
+on the caller's stream. PyTorch supplies device memory and streams.
 
 The library is built in-tree (``python -m paged_kv_gqa_amd._build``); importing
 this package without it raises ImportError - there is no fallback path.
@@ -61,6 +62,7 @@ class DecodeArgs(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
         ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("tile_tokens", ctypes.c_int),
         ("num_workers", ctypes.c_int), ("scale", ctypes.c_float),
+        ("tile_tokens_dev", ctypes.c_void_p),
     ]
 
 
@@ -83,6 +85,15 @@ def _load():
         "pkv_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_size_t)]),
         "pkv_decode_partial": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
+        "pkv_plan_device_scratch_bytes": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                         ctypes.c_int64,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
+        "pkv_plan_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
         "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -202,7 +213,7 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
                        req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
                        batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
                        kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
-                       stream=None):
+                       tile_tokens_dev=None, stream=None):
     """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
@@ -218,7 +229,31 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
     a.head_dim, a.page_size, a.bt_stride = head_dim, page_size, bt_stride
     a.kv_format = KV_FORMATS.get(kv_format, kv_format)
     a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
+    a.tile_tokens_dev = _ptr(tile_tokens_dev, "tile_tokens_dev")
     _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
+
+
+def pkv_plan_device_scratch_bytes(batch, num_kv_heads, page_size, kv_format, tile_tokens,
+                                  num_workers, max_items):
+    out = ctypes.c_size_t()
+    _check(_lib.pkv_plan_device_scratch_bytes(batch, num_kv_heads, page_size,
+                                              KV_FORMATS.get(kv_format, kv_format), tile_tokens,
+                                              num_workers, max_items, ctypes.byref(out)),
+           "pkv_plan_device_scratch_bytes")
+    return out.value
+
+
+def pkv_plan_device(*, seq_lens, batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size,
+                    kv_format, tile_tokens, num_workers, max_items, items, worker_offsets,
+                    req_tile_base, info, scratch, scratch_bytes, stream=None):
+    """Enqueue the device-side planner (same work list as pkv_plan, built on the GPU)."""
+    _check(_lib.pkv_plan_device(_ptr(seq_lens, "seq_lens"), batch, q_len, num_q_heads, num_kv_heads,
+                                head_dim, page_size, KV_FORMATS.get(kv_format, kv_format),
+                                tile_tokens, num_workers, max_items, _ptr(items, "items"),
+                                _ptr(worker_offsets, "worker_offsets"),
+                                _ptr(req_tile_base, "req_tile_base"), _ptr(info, "info"),
+                                _ptr(scratch, "scratch"), scratch_bytes, _stream_handle(stream)),
+           "pkv_plan_device")
 
 
 def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batch, q_len,
@@ -282,7 +317,8 @@ class PagedDecode:
     shape no allocation happens after the first steps."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
-                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3):
+                 q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3,
+                 device_plan=False, max_items=0):
         import torch
         self.torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
@@ -296,6 +332,12 @@ class PagedDecode:
         self._slot = 0
         self._workspace = None
         self.last_plan = None
+        # Device-built plan (pkv_plan_device): no host work per step, so the step can
+        # be captured in a graph. max_items is the plan's item capacity (0 = a bound
+        # derived from the block table's width).
+        self.device_plan = device_plan
+        self.max_items = max_items
+        self._dev = None
 
     def close(self):
         """Free the plan buffers (after the kernels that read them have completed)."""
@@ -343,6 +385,41 @@ class PagedDecode:
         self.last_plan = p
         return p
 
+    def default_capacity(self, batch, bt_stride):
+        """Item capacity of a device-built plan. For a fixed tile: the most items any
+        lengths up to bt_stride pages can need. For the automatic tile: room for the
+        largest candidate tile (65536) at any such lengths, plus 8 items per worker."""
+        max_len = bt_stride * self.page_size
+        H = self.num_kv_heads
+        if self.tile_tokens:
+            return batch * H * (-(-max_len // self.tile_tokens))
+        return 8 * self.num_workers + batch * H * (1 + -(-max_len // 65536))
+
+    def device_buffers(self, batch, bt_stride):
+        """The device plan's buffers for a batch size (allocated on first use)."""
+        torch = self.torch
+        cap = self.max_items or self.default_capacity(batch, bt_stride)
+        key = (batch, cap)
+        if self._dev is None or self._dev["key"] != key:
+            nscratch = pkv_plan_device_scratch_bytes(batch, self.num_kv_heads, self.page_size,
+                                                     self.kv_format, self.tile_tokens,
+                                                     self.num_workers, cap)
+            i32 = dict(dtype=torch.int32, device=self.device)
+            self._dev = dict(key=key, cap=cap, items=torch.empty((max(cap, 1), 4), **i32),
+                             offsets=torch.empty(self.num_workers + 1, **i32),
+                             rtb=torch.empty(batch + 1, **i32), info=torch.zeros(4, **i32),
+                             scratch=torch.empty(nscratch, dtype=torch.uint8, device=self.device),
+                             scratch_bytes=nscratch)
+        return self._dev
+
+    def plan_info(self):
+        """Status, tile, item count and most items per worker of the last device plan
+        (synchronises with the device)."""
+        if self._dev is None:
+            return None
+        st, T, N, mx = (int(x) for x in self._dev["info"].cpu())
+        return dict(status=st, T=T, N=N, max_items_per_worker=mx, capacity=self._dev["cap"])
+
     def workspace(self, num_partials):
         nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)
         if self._workspace is None or self._workspace.numel() < nbytes:
@@ -362,9 +439,26 @@ class PagedDecode:
                             v_scale=v_scale, seq_lens=seq_lens, out=out, lse_out=lse_out,
                             partial_events=partial_events)
         torch = self.torch
-        p = self.plan(seq_lens_h)
-        if seq_lens is None:
-            seq_lens = p["seq_lens"]
+        tile_dev = None
+        if self.device_plan:
+            if seq_lens is None or not getattr(seq_lens, "is_cuda", False):
+                raise ValueError("a device-built plan needs seq_lens as a CUDA int32 tensor")
+            B = int(seq_lens.shape[0])
+            d = self.device_buffers(B, block_table.shape[1])
+            pkv_plan_device(seq_lens=seq_lens, batch=B, q_len=self.q_len,
+                            num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
+                            head_dim=self.head_dim, page_size=self.page_size,
+                            kv_format=self.kv_format, tile_tokens=self.tile_tokens,
+                            num_workers=self.num_workers, max_items=d["cap"], items=d["items"],
+                            worker_offsets=d["offsets"], req_tile_base=d["rtb"], info=d["info"],
+                            scratch=d["scratch"], scratch_bytes=d["scratch_bytes"])
+            p = dict(T=self.tile_tokens, N=d["cap"], NP=d["cap"], W=self.num_workers, B=B, slot=None,
+                     items=d["items"], worker_offsets=d["offsets"], req_tile_base=d["rtb"])
+            tile_dev = d["info"][1:]
+        else:
+            p = self.plan(seq_lens_h)
+            if seq_lens is None:
+                seq_lens = p["seq_lens"]
         ws, ws_bytes = self.workspace(p["NP"])
         B = p["B"]
         if out is None:
@@ -380,7 +474,7 @@ class PagedDecode:
                            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
                            page_size=self.page_size, bt_stride=block_table.shape[1],
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
-                           scale=scale, k_scale=k_scale, v_scale=v_scale)
+                           scale=scale, k_scale=k_scale, v_scale=v_scale, tile_tokens_dev=tile_dev)
         if partial_events is not None:
             partial_events[1].record()
         pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
@@ -388,9 +482,10 @@ class PagedDecode:
                     num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
                     head_dim=self.head_dim, out=out, lse_out=lse_out)
         k = p["slot"]
-        if self._consumed[k] is None:
-            self._consumed[k] = torch.cuda.Event()
-        self._consumed[k].record()
+        if k is not None:
+            if self._consumed[k] is None:
+                self._consumed[k] = torch.cuda.Event()
+            self._consumed[k].record()
         return out
 
 

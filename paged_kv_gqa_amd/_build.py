@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["planner.cpp", "api.cpp", "decode_partial.hip", "combine.hip"]
+SOURCES = ["planner.cpp", "api.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip"]
 HEADERS = ["planner.hpp", "kernels.hpp"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

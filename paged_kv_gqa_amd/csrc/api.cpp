@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <string>
 
@@ -169,9 +170,11 @@ int pkv_workspace_bytes(int64_t num_partials, int rows_per_partial, int head_dim
 
 int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   if (a == nullptr) return fail(PKV_ERR_INVALID_ARG, "null args");
-  if (a->struct_size < sizeof(pkv_decode_args))
-    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size,
-                sizeof(pkv_decode_args));
+  // ABI 1 callers pass the struct without its last field.
+  constexpr size_t kV1Size = offsetof(pkv_decode_args, tile_tokens_dev);
+  if (a->struct_size < kV1Size)
+    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size, kV1Size);
+  const int32_t* tile_dev = a->struct_size >= sizeof(pkv_decode_args) ? a->tile_tokens_dev : nullptr;
   int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
                        a->kv_format);
   if (st != PKV_OK) return st;
@@ -180,9 +183,11 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   if (a->num_workers < 1) return fail(PKV_ERR_INVALID_ARG, "num_workers %d < 1", a->num_workers);
   const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
   const int64_t quantum = pkv::tile_quantum(a->page_size, fp8);
-  if (a->tile_tokens < 1 || a->tile_tokens % quantum != 0)
+  if (tile_dev == nullptr && (a->tile_tokens < 1 || a->tile_tokens % quantum != 0))
     return fail(PKV_ERR_UNSUPPORTED, "tile_tokens %d is not a positive multiple of %lld",
                 a->tile_tokens, static_cast<long long>(quantum));
+  if (tile_dev != nullptr && !aligned(tile_dev, 4))
+    return fail(PKV_ERR_ALIGNMENT, "tile_tokens_dev misaligned");
   if (a->num_items == 0) return PKV_OK;
   if (a->batch < 1 || a->num_pages < 1)
     return fail(PKV_ERR_INVALID_ARG, "work items given for an empty batch or cache");
@@ -229,12 +234,126 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   p.page_size = a->page_size;
   p.bt_stride = a->bt_stride;
   p.tile_tokens = a->tile_tokens;
+  p.tile_tokens_dev = tile_dev;
   p.qk_scale_log2 = a->scale * kLog2e;
   const hipError_t e = pkv::launch_decode_partial(p, a->head_dim, fp8, a->num_workers,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_partial launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }
+
+namespace {
+
+// Scratch of pkv_plan_device: candidate estimates and statuses, the remainder-item
+// placements of each plan being built and, for the automatic tile, one whole plan
+// per candidate tile.
+struct DevicePlanLayout {
+  size_t assign_off, plans_off, plan_stride, offsets_off, rtb_off, info_off, total;
+};
+
+DevicePlanLayout device_plan_layout(int batch, int Hkv, int W, int64_t max_items, int ncand) {
+  DevicePlanLayout l;
+  const size_t assign = 8 * static_cast<size_t>(batch) * Hkv;
+  l.assign_off = 256;
+  l.plans_off = align256(l.assign_off + assign * (ncand > 0 ? ncand : 1));
+  l.offsets_off = align256(16 * static_cast<size_t>(max_items > 0 ? max_items : 1));
+  l.rtb_off = l.offsets_off + align256(4 * (static_cast<size_t>(W) + 1));
+  l.info_off = l.rtb_off + align256(4 * (static_cast<size_t>(batch) + 1));
+  l.plan_stride = l.info_off + 256;
+  l.total = ncand > 0 ? l.plans_off + l.plan_stride * ncand : l.assign_off + assign;
+  return l;
+}
+
+}  // namespace
+
+int pkv_plan_device_scratch_bytes(int batch, int num_kv_heads, int page_size, int kv_format,
+                                  int tile_tokens, int num_workers, int64_t max_items,
+                                  size_t* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (batch < 0 || num_kv_heads < 1 || page_size < 1 || tile_tokens < 0 || num_workers < 1 ||
+      max_items < 0)
+    return fail(PKV_ERR_INVALID_ARG, "size out of range (batch %d, kv heads %d, P %d, T %d, W %d, "
+                "max_items %lld)", batch, num_kv_heads, page_size, tile_tokens, num_workers,
+                static_cast<long long>(max_items));
+  if (kv_format != PKV_KV_BF16 && kv_format != PKV_KV_FP8_E4M3FN)
+    return fail(PKV_ERR_INVALID_ARG, "kv_format %d is not a pkv_kv_format", kv_format);
+  const int ncand = tile_tokens == 0
+                        ? pkv::auto_tile_candidates(pkv::tile_quantum(page_size, kv_format != 0))
+                        : 0;
+  *out = device_plan_layout(batch, num_kv_heads, num_workers, max_items, ncand).total;
+  return PKV_OK;
+}
+
+int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_heads,
+                    int num_kv_heads, int head_dim, int page_size, int kv_format,
+                    int tile_tokens, int num_workers, int64_t max_items, int32_t* items,
+                    int32_t* worker_offsets, int32_t* req_tile_base, int32_t* info,
+                    void* scratch, size_t scratch_bytes, void* stream) {
+  int st = check_shape(q_len, num_q_heads, num_kv_heads, head_dim, page_size, kv_format);
+  if (st != PKV_OK) return st;
+  if (batch < 0 || num_workers < 1 || tile_tokens < 0 || max_items < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size (batch %d, W %d, T %d, max_items %lld)", batch,
+                num_workers, tile_tokens, static_cast<long long>(max_items));
+  if (batch > pkv::kMaxDevicePlanBatch || num_workers > pkv::kMaxDevicePlanWorkers ||
+      max_items > INT32_MAX / 4)
+    return fail(PKV_ERR_UNSUPPORTED, "device plan limits: batch %d (max %d), W %d (max %d), "
+                "max_items %lld", batch, pkv::kMaxDevicePlanBatch, num_workers,
+                pkv::kMaxDevicePlanWorkers, static_cast<long long>(max_items));
+  const bool fp8 = kv_format == PKV_KV_FP8_E4M3FN;
+  const int64_t quantum = pkv::tile_quantum(page_size, fp8);
+  if (tile_tokens % quantum != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "tile_tokens %d is not a multiple of the quantum %lld",
+                tile_tokens, static_cast<long long>(quantum));
+  if ((batch > 0 && seq_lens == nullptr) || items == nullptr || worker_offsets == nullptr ||
+      req_tile_base == nullptr || info == nullptr || scratch == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(items, 16) || !aligned(scratch, 16) || !aligned(seq_lens, 4) ||
+      !aligned(worker_offsets, 4) || !aligned(req_tile_base, 4) || !aligned(info, 4))
+    return fail(PKV_ERR_ALIGNMENT, "items and scratch need 16 bytes, int32 arrays 4");
+  const int ncand = tile_tokens == 0 ? pkv::auto_tile_candidates(quantum) : 0;
+  if (ncand > pkv::kMaxDevicePlanCandidates)
+    return fail(PKV_ERR_UNSUPPORTED, "too many candidate tiles");
+  const DevicePlanLayout lay = device_plan_layout(batch, num_kv_heads, num_workers, max_items, ncand);
+  if (scratch_bytes < lay.total)
+    return fail(PKV_ERR_WORKSPACE, "scratch %zu bytes < %zu needed", scratch_bytes, lay.total);
+
+  pkv::DevicePlanParams p;
+  p.seq_lens = seq_lens;
+  p.items = items;
+  p.worker_offsets = worker_offsets;
+  p.req_tile_base = req_tile_base;
+  p.info = info;
+  p.cand_est = static_cast<long long*>(scratch);
+  p.cand_status = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) +
+                                             8 * pkv::kMaxDevicePlanCandidates);
+  p.scratch_assign = reinterpret_cast<int2*>(static_cast<char*>(scratch) + lay.assign_off);
+  p.cand_plans = static_cast<char*>(scratch) + lay.plans_off;
+  p.cand_stride = static_cast<long long>(lay.plan_stride);
+  p.cand_offsets_off = static_cast<long long>(lay.offsets_off);
+  p.cand_rtb_off = static_cast<long long>(lay.rtb_off);
+  p.cand_info_off = static_cast<long long>(lay.info_off);
+  p.max_items = max_items;
+  p.tile_tokens = tile_tokens;
+  p.kv_bytes_per_token = 2LL * head_dim * (fp8 ? 1 : 2);
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_kv_heads = num_kv_heads;
+  p.num_workers = num_workers;
+  p.quantum = static_cast<int>(quantum);
+  p.num_candidates = pkv::auto_tile_candidates(quantum);
+  p.rows = (num_q_heads / num_kv_heads) * q_len;
+  p.head_dim = head_dim;
+  const hipError_t e = pkv::launch_plan_device(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "plan_device launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+static_assert(pkv::PKV_DEV_OK == PKV_OK && pkv::PKV_DEV_ERR_SEQ == PKV_ERR_SEQ &&
+                  pkv::PKV_DEV_ERR_UNSUPPORTED == PKV_ERR_UNSUPPORTED &&
+                  pkv::PKV_DEV_ERR_WORKSPACE == PKV_ERR_WORKSPACE,
+              "device status codes are the pkv_status values");
+static_assert(8 * pkv::kMaxDevicePlanCandidates + 4 * pkv::kMaxDevicePlanCandidates <= 256,
+              "candidate scratch fits the first 256 bytes");
 
 int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_partials,
                 const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,

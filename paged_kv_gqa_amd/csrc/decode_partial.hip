@@ -337,9 +337,13 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     const uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ worker_offsets, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, const DecodeShape sh) {
+    const int32_t* __restrict__ worker_offsets, const int32_t* __restrict__ tile_dev,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, const DecodeShape sh_arg) {
   using C = Cfg<D, FP8>;
+  // The tile size comes from the launch, or from device memory when a device-built
+  // plan chose it.
+  DecodeShape sh = sh_arg;
+  if (tile_dev != nullptr) sh.tile_tokens = __builtin_amdgcn_readfirstlane(tile_dev[0]);
   // Each wave's region stages its chunks and, after its last chunk of an item,
   // holds its unnormalised output rows [16][D] for the merge.
   __shared__ u32x4 lds_stage[kWaves][C::kStageVec];
@@ -514,7 +518,7 @@ hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8, 
 #define PKV_LAUNCH(DIM, F8)                                                                   \
   hipLaunchKernelGGL((decode_partial_kernel<DIM, F8>), grid, block, 0, stream, p.q, p.k_cache, \
                      p.v_cache, p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items,     \
-                     p.worker_offsets, p.ws_o, p.ws_lse, sh)
+                     p.worker_offsets, p.tile_tokens_dev, p.ws_o, p.ws_lse, sh)
   if (head_dim == 128) {
     if (fp8)
       PKV_LAUNCH(128, true);

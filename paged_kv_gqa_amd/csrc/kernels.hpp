@@ -26,6 +26,7 @@ struct DecodeParams {
   const int32_t* worker_offsets;
   float* ws_o;                // [num_partials, M, D]
   float* ws_lse;              // [num_partials, M]
+  const int32_t* tile_tokens_dev;  // if set, T is read from here instead of tile_tokens
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
   float qk_scale_log2;        // softmax scale * log2(e)
 };
@@ -38,6 +39,38 @@ struct CombineParams {
   float* lse_out;                // [B, Tq, Hq] or null
   int batch, q_len, num_q_heads, num_kv_heads, group, rows;
 };
+
+// Device planner limits: one thread per worker, the requests sorted in LDS.
+constexpr int kMaxDevicePlanWorkers = 1024;
+constexpr int kMaxDevicePlanBatch = 4096;
+// Candidate tiles of the automatic rule: quantum << c, c < num_candidates <= 16.
+constexpr int kMaxDevicePlanCandidates = 16;
+
+// Status codes the device planner writes (the pkv_status values).
+constexpr int PKV_DEV_OK = 0;
+constexpr int PKV_DEV_ERR_UNSUPPORTED = -2;
+constexpr int PKV_DEV_ERR_WORKSPACE = -4;
+constexpr int PKV_DEV_ERR_SEQ = -6;
+
+struct DevicePlanParams {
+  const int32_t* seq_lens;    // device [B]
+  int32_t* items;             // [max_items][4]
+  int32_t* worker_offsets;    // [W + 1]
+  int32_t* req_tile_base;     // [B + 1]
+  int32_t* info;              // [4] status, T, N, most items on one worker
+  long long* cand_est;        // scratch [kMaxDevicePlanCandidates]
+  int32_t* cand_status;       // scratch [kMaxDevicePlanCandidates]
+  int2* scratch_assign;       // scratch [candidates][B * Hkv]: (worker, position) of
+                              // each remainder item
+  char* cand_plans;           // scratch: one plan per candidate tile (automatic tile)
+  long long cand_stride, cand_offsets_off, cand_rtb_off, cand_info_off;
+  long long max_items;
+  long long tile_tokens;      // 0 = automatic
+  long long kv_bytes_per_token;
+  int batch, q_len, num_kv_heads, num_workers, quantum, num_candidates, rows, head_dim;
+};
+
+hipError_t launch_plan_device(const DevicePlanParams& p, hipStream_t stream);
 
 hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8,
                                  int num_workers, hipStream_t stream);

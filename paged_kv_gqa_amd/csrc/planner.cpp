@@ -138,6 +138,12 @@ int64_t tile_quantum(int page_size, bool fp8) {
   return static_cast<int64_t>(page_size) * 64 / std::gcd(page_size, 64);
 }
 
+int auto_tile_candidates(int64_t quantum) {
+  int n = 1;
+  for (int64_t T = quantum; T * 2 <= kMaxAutoTile; T *= 2) ++n;
+  return n;
+}
+
 namespace {
 
 // Expects split_requests(T) to have filled s.nfull / s.rem.
@@ -182,10 +188,8 @@ int64_t auto_tile_tokens(int batch, const int32_t* seq_lens, int q_len, int num_
   }
   total *= Hkv;
   std::vector<int64_t> cands;
-  for (int64_t T = quantum;; T *= 2) {
-    cands.push_back(T);
-    if (T * 2 > kMaxAutoTile) break;
-  }
+  const int ncand = auto_tile_candidates(quantum);
+  for (int k = 0; k < ncand; ++k) cands.push_back(quantum << k);
   // Candidates are quantum * 2^k, so floor(L / T) = floor(L / quantum) >> k.
   Scratch s;
   std::vector<int32_t> lq(batch);

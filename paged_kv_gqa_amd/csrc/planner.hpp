@@ -19,6 +19,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile-size quantum: the page size for bf16, lcm(page size, 64) for fp8.
 int64_t tile_quantum(int page_size, bool fp8);
 
+// Number of candidate tiles of the automatic rule: quantum * 2^k <= 65536, k >= 0
+// (at least the quantum itself).
+int auto_tile_candidates(int64_t quantum);
+
 // Loads and item counts of the plan for tile size T without materialising it.
 PlanStats plan_stats(int batch, const int32_t* seq_lens, int num_kv_heads, int64_t T,
                      int W);

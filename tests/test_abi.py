@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -195,6 +195,80 @@ def test_host_arrays_are_not_device_arguments(name):
         pkv.pkv_combine(workspace=9 * A, workspace_bytes=1 << 30, num_partials=4, req_tile_base=8 * A,
                         batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
                         out=np.zeros(8, np.uint16), stream=0)
+
+
+def test_abi1_struct_size_is_accepted():
+    """A caller built against ABI 1 passes the struct without tile_tokens_dev."""
+    v1 = pkv.DecodeArgs.tile_tokens_dev.offset
+    a = pkv.DecodeArgs()
+    kw = decode_kwargs(num_items=0, num_partials=0)
+    for name in ("batch", "q_len", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
+                 "bt_stride", "tile_tokens", "num_workers", "scale"):
+        setattr(a, name, kw[name])
+    a.tile_tokens_dev = 8 * A            # beyond an ABI 1 struct: must not be read
+    a.struct_size = v1
+    assert pkv._lib.pkv_decode_partial(ctypes.byref(a), None) == pkv.PKV_OK
+    a.struct_size = v1 - 8
+    assert pkv._lib.pkv_decode_partial(ctypes.byref(a), None) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_device_tile_replaces_the_host_tile_check():
+    # tile_tokens 24 is no multiple of 16, but with tile_tokens_dev it is not used
+    pkv.pkv_decode_partial(**decode_kwargs(num_items=0, num_partials=0, tile_tokens=24,
+                                           tile_tokens_dev=10 * A))
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode_partial(**decode_kwargs(tile_tokens_dev=10 * A + 2))
+    assert e.value.status == pkv.PKV_ERR_ALIGNMENT
+
+
+def test_plan_device_scratch_bytes():
+    # fixed tile: the candidate block plus one placement per remainder item
+    assert pkv.pkv_plan_device_scratch_bytes(0, 8, 16, "bf16", 64, 512, 100) == 256
+    assert pkv.pkv_plan_device_scratch_bytes(128, 8, 16, "bf16", 64, 512, 100) == 256 + 8 * 128 * 8
+    # automatic tile: 13 candidates (16 .. 65536), each with placements and a whole plan
+    r = lambda x: (x + 255) // 256 * 256
+    B, H, W, cap = 128, 8, 512, 1000
+    plan = r(16 * cap) + r(4 * (W + 1)) + r(4 * (B + 1)) + 256
+    assert pkv.pkv_plan_device_scratch_bytes(B, H, 16, "bf16", 0, W, cap) == \
+        r(256 + 13 * 8 * B * H) + 13 * plan
+    # fp8 (quantum 64): 11 candidates
+    assert pkv.pkv_plan_device_scratch_bytes(B, H, 64, "fp8", 0, W, cap) == \
+        r(256 + 11 * 8 * B * H) + 11 * plan
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_plan_device_scratch_bytes(-1, 8, 16, "bf16", 0, 512, 10)
+
+
+def plan_device_kwargs(**kw):
+    base = dict(seq_lens=A, batch=4, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                page_size=16, kv_format="bf16", tile_tokens=0, num_workers=512, max_items=100,
+                items=2 * A, worker_offsets=3 * A, req_tile_base=4 * A, info=5 * A, scratch=6 * A,
+                scratch_bytes=1 << 20, stream=0)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_workers=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_workers=1025), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(batch=4097), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(batch=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(max_items=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(max_items=1 << 30), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(tile_tokens=-16), pkv.PKV_ERR_INVALID_ARG),
+    (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),          # fp8 needs page size 64
+    (dict(info=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(seq_lens=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(items=2 * A + 4), pkv.PKV_ERR_ALIGNMENT),
+    (dict(scratch=6 * A + 8), pkv.PKV_ERR_ALIGNMENT),
+    (dict(tile_tokens=64, scratch_bytes=256 + 8 * 4 * 2 - 1), pkv.PKV_ERR_WORKSPACE),
+    (dict(scratch_bytes=1000), pkv.PKV_ERR_WORKSPACE),
+])
+def test_plan_device_argument_errors(kw, status):
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_device(**plan_device_kwargs(**kw))
+    assert e.value.status == status
 
 
 @pytest.mark.parametrize("kw,status", [
