@@ -25,6 +25,13 @@ Readings of points the pages leave open (each also listed in the design notes):
 
 Everything is evaluated in float64 from the exact stored values (bf16 bits and
 e4m3fn codes decode exactly; code * fp32 scale is exact in float64).
+
+Block-sparse decode (the HALOps review's sparse attention: a precomputed block mask,
+masked-out KV tiles skipped, per-tile FP8 scaling kept). Readings: one mask entry per
+(request, kv head, logical page), nonzero = attended; the pages that hold the step's
+own query tokens (positions L-Tq .. L-1) are always attended, so a query always
+sees itself. The key set of row t is then
+  { j <= pos : block_mask[b, g, j // P] != 0  or  j // P >= (L - Tq) // P }.
 """
 
 import numpy as np
@@ -44,12 +51,20 @@ def gather_kv(cache, scales, block_table_row, L, g, page_size, kv_format):
     return x.reshape(n_pages * page_size, -1)[:L]
 
 
-def decode_attention(inp, pairs=None):
+def sparse_keys(mask_row, L, q_len, pos, page_size):
+    """Positions j <= pos attended under one (request, kv head) block-mask row."""
+    first_query_page = (L - q_len) // page_size
+    return [j for j in range(pos + 1)
+            if mask_row[j // page_size] != 0 or j // page_size >= first_query_page]
+
+
+def decode_attention(inp, pairs=None, block_mask=None):
     """Reference decode attention for a ``synth.DecodeInputs`` batch.
 
     Returns (out, lse): out float64 [B, Tq, Hq, D], lse float64 [B, Tq, Hq] (natural
     log). With ``pairs`` (an iterable of (b, g)), only those request / kv-head groups
-    are computed and every other entry is NaN.
+    are computed and every other entry is NaN. ``block_mask`` (uint8 [B, Hkv, >=
+    pages]) restricts the keys to the attended pages (block-sparse decode).
     """
     B, Tq = inp.batch, inp.q_len
     Hq, Hkv, D, P = inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size
@@ -66,7 +81,11 @@ def decode_attention(inp, pairs=None):
         V = gather_kv(inp.v_cache, inp.v_scale, inp.block_table[b], L, g, P, inp.kv_format)
         for t in range(Tq):
             pos = L - Tq + t
-            Kt, Vt = K[:pos + 1], V[:pos + 1]
+            if block_mask is None:
+                Kt, Vt = K[:pos + 1], V[:pos + 1]
+            else:
+                idx = sparse_keys(block_mask[b, g], L, Tq, pos, P)
+                Kt, Vt = K[idx], V[idx]
             qh = q[b, t, g * G:(g + 1) * G, :]          # [G, D]
             s = scale * (qh @ Kt.T)                     # [G, pos+1]
             mx = s.max(axis=1, keepdims=True)

@@ -198,6 +198,49 @@ def apply_poison(inp):
     return inp
 
 
+def make_block_mask(inp, keep, seed=1):
+    """Block mask for block-sparse decode: uint8 [B, Hkv, bt_stride], 1 = page
+    attended, each (request, kv head, logical page) kept with probability ``keep``
+    (its own generator, so the inputs of ``make_inputs`` are unchanged)."""
+    rng = np.random.default_rng(seed)
+    shape = (inp.batch, inp.num_kv_heads, inp.block_table.shape[1])
+    return (rng.random(shape) < keep).astype(np.uint8)
+
+
+def attended_pages(inp, block_mask):
+    """Per (request, kv head): the logical pages block-sparse decode reads - the
+    masked-in pages plus those holding the step's query tokens. List of lists."""
+    P, Tq = inp.page_size, inp.q_len
+    out = []
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        n = (L + P - 1) // P
+        first_query_page = (L - Tq) // P
+        out.append([[p for p in range(n) if block_mask[b, g, p] or p >= first_query_page]
+                    for g in range(inp.num_kv_heads)])
+    return out
+
+
+def sparse_algorithmic_bytes(inp, block_mask):
+    """Bytes a block-sparse decode step must move at minimum: K and V of the
+    attended tokens, Q, the bf16 output, the mask entries and block-table entries of
+    every page, seq_lens and (fp8) the scales of attended pages."""
+    eb = 2 if inp.kv_format == "bf16" else 1
+    P = inp.page_size
+    tokens = pages_att = pages_all = 0
+    for b, per_g in enumerate(attended_pages(inp, block_mask)):
+        L = int(inp.seq_lens[b])
+        n = (L + P - 1) // P
+        pages_all += n
+        for pages in per_g:
+            pages_att += len(pages)
+            tokens += sum(min(P, L - p * P) for p in pages)
+    kv = tokens * inp.head_dim * eb * 2
+    q = inp.batch * inp.q_len * inp.num_q_heads * inp.head_dim * 2
+    scales = 0 if inp.kv_format == "bf16" else 2 * 4 * pages_att
+    return kv + 2 * q + 4 * pages_all + pages_all * inp.num_kv_heads + 4 * inp.batch + scales
+
+
 def algorithmic_bytes(inp):
     """Bytes the decode step must move at minimum: K and V of every valid token,
     Q, the bf16 output, the block-table entries used, seq_lens and (fp8) the scales
