@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-sparse", type=float, default=None, metavar="KEEP",
+                    help="block-sparse decode: each (request, kv head, page) attended with "
+                         "probability KEEP (seeded), plus the pages of the query tokens")
     ap.add_argument("--device-plan", action="store_true",
                     help="build the plan on the GPU (pkv_plan_device) from device seq_lens "
                          "instead of on the host")
@@ -106,9 +109,15 @@ def main():
     cfg = synth.ALL[args.workload]
     log("generating %s inputs (seed %d)" % (args.workload, args.seed))
     inp = synth.make_inputs(cfg, seed=args.seed)
-    algo = synth.algorithmic_bytes(inp)
     out_bytes = inp.batch * inp.q_len * inp.num_q_heads * inp.head_dim * 2
-    partial_algo = algo - out_bytes          # what decode_partial itself must move
+    mask_h = mask_d = None
+    if args.block_sparse is not None:
+        mask_h = synth.make_block_mask(inp, args.block_sparse, seed=1)
+        algo = synth.sparse_algorithmic_bytes(inp, mask_h)
+        partial_algo = synth.sparse_algorithmic_bytes(inp, mask_h, decode_only=True)
+    else:
+        algo = synth.algorithmic_bytes(inp)
+        partial_algo = algo - out_bytes          # what decode_partial itself must move
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -123,6 +132,8 @@ def main():
         vs = torch.from_numpy(inp.v_scale).to(dev)
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl_dev = torch.from_numpy(inp.seq_lens).to(dev)
+    if mask_h is not None:
+        mask_d = torch.from_numpy(mask_h).to(dev)
     seq_lens_h = inp.seq_lens.copy()
     runner = pkv.PagedDecode(num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
                              head_dim=inp.head_dim, page_size=inp.page_size,
@@ -134,7 +145,7 @@ def main():
 
     def step(events=None):
         runner(q, k, v, bt, seq_lens_h, inp.scale, k_scale=ks, v_scale=vs, seq_lens=sl_dev,
-               out=out, partial_events=events)
+               out=out, partial_events=events, block_mask=mask_d, block_mask_h=mask_h)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
@@ -149,6 +160,8 @@ def main():
     else:
         plan = runner.last_plan
         step_desc = "host plan (read in place by the kernels) + decode_partial + combine"
+    if mask_h is not None:
+        step_desc = "block mask compaction + " + step_desc
     log("plan: tile %d tokens, %d items, %d workers" % (plan["T"], plan["N"], plan["W"]))
 
     K = args.steps
@@ -165,7 +178,7 @@ def main():
     ms_per_step = wall / K * 1e3
     value = algo / (wall / K) / 1e9
     achieved = partial_algo / kern_avg_s / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload) if mask_h is None else None
     log("%.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s); decode_partial %.1f us avg (%.1f GB/s)" % (
         ms_per_step * 1e3, value, 100 * value / HBM_PEAK_GBS, kern_avg_s * 1e6, achieved))
 
@@ -185,7 +198,10 @@ def main():
         "dtype": inp.kv_format,
         "data": "synthetic",
         "config": {
-            "workload": cfg["desc"],
+            "workload": cfg["desc"] + ("" if mask_h is None else
+                                       "; block-sparse: each (request, kv head, page) attended "
+                                       "with probability %g (seed 1) plus the query pages"
+                                       % args.block_sparse),
             "batch": inp.batch,
             "sum_seq_lens": int(inp.seq_lens.sum()),
             "q_len": inp.q_len,

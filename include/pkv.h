@@ -160,6 +160,11 @@ typedef struct pkv_decode_args {
    * then not checked): pass info + 1 of pkv_plan_device. A struct_size that ends
    * before this field (an ABI 1 caller) means NULL. */
   const int32_t* tile_tokens_dev;
+  /* ABI 2. Request split V >= 1 (0 and a struct_size ending before this field mean
+   * 1): request b of the work list is part b % V of the caller's request b / V, and q
+   * is [batch / V, Tq, V * num_q_heads, D]. Block-sparse decode uses V = Hkv with one
+   * kv head per part (see pkv_block_sparse_compact); V = 1 is the layout above. */
+  int request_split;
 } pkv_decode_args;
 
 /*
@@ -232,6 +237,54 @@ int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_hea
 int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_partials,
                 const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
                 int num_kv_heads, int head_dim, void* out, float* lse_out, void* stream);
+
+/* pkv_combine for a work list whose requests are split in V parts (request_split of
+ * pkv_decode_args): out is [batch / V, Tq, V * num_q_heads, D] and lse_out
+ * [batch / V, Tq, V * num_q_heads]. V = 1 is pkv_combine. Errors: as pkv_combine, and
+ * INVALID_ARG when V < 1 or batch % V != 0. */
+int pkv_combine_split(const void* workspace, size_t workspace_bytes, int64_t num_partials,
+                      const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
+                      int num_kv_heads, int head_dim, int request_split, void* out,
+                      float* lse_out, void* stream);
+
+/*
+ * Block-sparse decode (the HALOps review's sparse attention: a precomputed block mask,
+ * masked-out KV tiles skipped, per-tile FP8 scaling kept). The mask has one byte per
+ * (request, kv head, logical page), nonzero = attended; the pages holding the step's
+ * query tokens (positions L_b - Tq .. L_b - 1) are attended whatever their byte. Row t
+ * of request b then attends to the keys j <= L_b - Tq + t whose page is attended.
+ *
+ * pkv_block_sparse_compact (enqueued) turns this into a dense one-kv-head problem of
+ * batch * Hkv requests, request v = b * Hkv + g holding the attended pages of kv head
+ * g of request b:
+ *   block_table   device int32 [batch, bt_stride] (the caller's)
+ *   seq_lens      device int32 [batch]
+ *   block_mask    device uint8 [batch, Hkv, mask_stride], mask_stride >= bt_stride
+ *   bt_out        device int32 [batch * Hkv, bt_stride]: row v lists phys * Hkv + g
+ *                 of its attended pages in logical order (later entries untouched)
+ *   seq_lens_out  device int32 [batch * Hkv]: attended tokens of row v (L_b minus
+ *                 P per masked page); an invalid L_b is passed on unchanged
+ * The one-kv-head problem reads the same cache viewed as [num_pages * Hkv, 1, P, D]
+ * (scales as [num_pages * Hkv, 1]): plan it with num_kv_heads = 1, num_q_heads = G
+ * and the seq_lens_out lengths (pkv_block_sparse_lengths computes them on the host),
+ * run pkv_decode_partial with batch * Hkv requests, num_pages * Hkv pages, bt_out,
+ * seq_lens_out and request_split = Hkv, then pkv_combine_split with request_split =
+ * Hkv; out and lse_out keep the caller's [batch, Tq, Hq, ...] layout.
+ * Errors: INVALID_ARG (null pointer, sizes), UNSUPPORTED (num_pages * Hkv >= 2^31
+ * cannot be addressed), ALIGNMENT (int32 arrays), HIP.
+ */
+int pkv_block_sparse_compact(const int32_t* block_table, const int32_t* seq_lens,
+                             const uint8_t* block_mask, int batch, int num_kv_heads,
+                             int q_len, int page_size, int bt_stride, int mask_stride,
+                             int64_t num_pages, int32_t* bt_out, int32_t* seq_lens_out,
+                             void* stream);
+
+/* Host twin of pkv_block_sparse_compact's lengths: lengths_out_h int32 [batch *
+ * num_kv_heads] from host seq_lens and a host mask of the same layout, for planning on
+ * the host. Errors: INVALID_ARG, SEQ (some L_b < max(1, q_len)). */
+int pkv_block_sparse_lengths(int batch, const int32_t* seq_lens_h, const uint8_t* block_mask_h,
+                             int num_kv_heads, int q_len, int page_size, int mask_stride,
+                             int32_t* lengths_out_h);
 
 #ifdef __cplusplus
 }

@@ -62,7 +62,7 @@ class DecodeArgs(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
         ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("tile_tokens", ctypes.c_int),
         ("num_workers", ctypes.c_int), ("scale", ctypes.c_float),
-        ("tile_tokens_dev", ctypes.c_void_p),
+        ("tile_tokens_dev", ctypes.c_void_p), ("request_split", ctypes.c_int),
     ]
 
 
@@ -94,6 +94,16 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "pkv_combine_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
+        "pkv_block_sparse_compact": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+        "pkv_block_sparse_lengths": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_void_p, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]),
         "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -213,7 +223,7 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
                        req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
                        batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
                        kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
-                       tile_tokens_dev=None, stream=None):
+                       tile_tokens_dev=None, request_split=1, stream=None):
     """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
@@ -230,6 +240,7 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
     a.kv_format = KV_FORMATS.get(kv_format, kv_format)
     a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
     a.tile_tokens_dev = _ptr(tile_tokens_dev, "tile_tokens_dev")
+    a.request_split = request_split
     _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
 
 
@@ -263,6 +274,41 @@ def pkv_combine(*, workspace, workspace_bytes, num_partials, req_tile_base, batc
                             _ptr(req_tile_base, "req_tile_base"), batch, q_len, num_q_heads,
                             num_kv_heads, head_dim, _ptr(out, "out"), _ptr(lse_out, "lse_out"),
                             _stream_handle(stream)), "pkv_combine")
+
+
+def pkv_combine_split(*, workspace, workspace_bytes, num_partials, req_tile_base, batch, q_len,
+                      num_q_heads, num_kv_heads, head_dim, request_split, out, lse_out=None,
+                      stream=None):
+    """Enqueue the combine for a work list whose requests are split in parts."""
+    _check(_lib.pkv_combine_split(_ptr(workspace, "workspace"), workspace_bytes, num_partials,
+                                  _ptr(req_tile_base, "req_tile_base"), batch, q_len, num_q_heads,
+                                  num_kv_heads, head_dim, request_split, _ptr(out, "out"),
+                                  _ptr(lse_out, "lse_out"), _stream_handle(stream)),
+           "pkv_combine_split")
+
+
+def pkv_block_sparse_compact(*, block_table, seq_lens, block_mask, batch, num_kv_heads, q_len,
+                             page_size, bt_stride, mask_stride, num_pages, bt_out, seq_lens_out,
+                             stream=None):
+    """Enqueue the block-mask compaction into a one-kv-head problem (see include/pkv.h)."""
+    _check(_lib.pkv_block_sparse_compact(_ptr(block_table, "block_table"), _ptr(seq_lens, "seq_lens"),
+                                         _ptr(block_mask, "block_mask"), batch, num_kv_heads, q_len,
+                                         page_size, bt_stride, mask_stride, num_pages,
+                                         _ptr(bt_out, "bt_out"), _ptr(seq_lens_out, "seq_lens_out"),
+                                         _stream_handle(stream)),
+           "pkv_block_sparse_compact")
+
+
+def pkv_block_sparse_lengths(seq_lens_h, block_mask_h, num_kv_heads, q_len, page_size):
+    """Host lengths of the compacted one-kv-head problem: int32 [B * num_kv_heads]."""
+    sl, slp = _i32(seq_lens_h)
+    m = np.ascontiguousarray(block_mask_h, dtype=np.uint8)
+    B = len(sl)
+    out = np.empty(B * num_kv_heads, np.int32)
+    _check(_lib.pkv_block_sparse_lengths(B, slp, m.ctypes.data, num_kv_heads, q_len, page_size,
+                                         m.shape[-1], out.ctypes.data_as(_i32p)),
+           "pkv_block_sparse_lengths")
+    return out
 
 
 # ---------------------------------------------------------------------------------
@@ -307,14 +353,22 @@ class HostPlanBuffer:
 
 
 class PagedDecode:
-    """One decode step = host plan + decode_partial + combine, enqueued on the current
-    torch stream with no host synchronisation.
+    """One decode step = plan + decode_partial + combine, enqueued on the current torch
+    stream with no host synchronisation.
 
-    The plan is written into a ring of coherent pinned buffers that the kernels read
-    directly (no host-to-device copy on the step's critical path). A buffer is
-    rewritten only after the kernels of the step that last read it have completed
-    (an event per buffer). The workspace grows on demand and is kept, so at a fixed
-    shape no allocation happens after the first steps."""
+    Host plan (default): the plan is written into a ring of coherent pinned buffers
+    that the kernels read directly (no host-to-device copy on the step's critical
+    path). A buffer is rewritten only after the kernels of the step that last read it
+    have completed (an event per buffer).
+    Device plan (``device_plan=True``): ``pkv_plan_device`` builds the same plan on
+    the GPU from device seq_lens, so the step needs no host lengths and can be
+    captured in a graph.
+    Block-sparse decode: pass ``block_mask`` (device uint8 [B, Hkv, >= bt_stride]); the
+    step compacts it (``pkv_block_sparse_compact``) into a one-kv-head problem of
+    B * Hkv requests and runs the same kernels on it. It is planned on the host when the
+    host copy ``block_mask_h`` is given (for the lengths), else on the device.
+    The workspace and device buffers grow on demand and are kept, so at a fixed shape
+    no allocation happens after the first steps."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
                  q_len=1, tile_tokens=0, num_workers=0, device=None, slots=3,
@@ -338,6 +392,7 @@ class PagedDecode:
         self.device_plan = device_plan
         self.max_items = max_items
         self._dev = None
+        self._sparse = None
 
     def close(self):
         """Free the plan buffers (after the kernels that read them have completed)."""
@@ -355,11 +410,14 @@ class PagedDecode:
         except Exception:  # noqa: BLE001  (interpreter shutdown: the process releases it)
             pass
 
-    def plan(self, seq_lens_h):
-        """Host plan into the next plan buffer; returns a dict describing it."""
+    def plan(self, seq_lens_h, num_q_heads=None, num_kv_heads=None):
+        """Host plan into the next plan buffer; returns a dict describing it. The head
+        counts default to the runner's (block-sparse steps plan a one-kv-head problem)."""
+        Hq = num_q_heads or self.num_q_heads
+        Hkv = num_kv_heads or self.num_kv_heads
         sl = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
-        T, N, NP = pkv_plan_query(sl, self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim,
-                                  self.page_size, self.kv_format, self.tile_tokens, self.num_workers)
+        T, N, NP = pkv_plan_query(sl, self.q_len, Hq, Hkv, self.head_dim, self.page_size,
+                                  self.kv_format, self.tile_tokens, self.num_workers)
         W, B = self.num_workers, len(sl)
         n_off = 4 * N
         n_rtb = n_off + _round4(W + 1)
@@ -376,7 +434,7 @@ class PagedDecode:
             buf = HostPlanBuffer(4 * max(total, 1024))
             self._bufs[k] = buf
         h = buf.array
-        pkv_plan(sl, self.q_len, self.num_kv_heads, T, W,
+        pkv_plan(sl, self.q_len, Hkv, T, W,
                  out=(h[:n_off].reshape(N, 4), h[n_off:n_off + W + 1], h[n_rtb:n_rtb + B + 1]))
         h[n_sl:n_sl + B] = sl
         a = buf.addr
@@ -385,25 +443,25 @@ class PagedDecode:
         self.last_plan = p
         return p
 
-    def default_capacity(self, batch, bt_stride):
+    def default_capacity(self, batch, bt_stride, num_kv_heads=None):
         """Item capacity of a device-built plan. For a fixed tile: the most items any
         lengths up to bt_stride pages can need. For the automatic tile: room for the
         largest candidate tile (65536) at any such lengths, plus 8 items per worker."""
         max_len = bt_stride * self.page_size
-        H = self.num_kv_heads
+        H = num_kv_heads or self.num_kv_heads
         if self.tile_tokens:
             return batch * H * (-(-max_len // self.tile_tokens))
         return 8 * self.num_workers + batch * H * (1 + -(-max_len // 65536))
 
-    def device_buffers(self, batch, bt_stride):
+    def device_buffers(self, batch, bt_stride, num_kv_heads=None):
         """The device plan's buffers for a batch size (allocated on first use)."""
         torch = self.torch
-        cap = self.max_items or self.default_capacity(batch, bt_stride)
-        key = (batch, cap)
+        H = num_kv_heads or self.num_kv_heads
+        cap = self.max_items or self.default_capacity(batch, bt_stride, H)
+        key = (batch, H, cap)
         if self._dev is None or self._dev["key"] != key:
-            nscratch = pkv_plan_device_scratch_bytes(batch, self.num_kv_heads, self.page_size,
-                                                     self.kv_format, self.tile_tokens,
-                                                     self.num_workers, cap)
+            nscratch = pkv_plan_device_scratch_bytes(batch, H, self.page_size, self.kv_format,
+                                                     self.tile_tokens, self.num_workers, cap)
             i32 = dict(dtype=torch.int32, device=self.device)
             self._dev = dict(key=key, cap=cap, items=torch.empty((max(cap, 1), 4), **i32),
                              offsets=torch.empty(self.num_workers + 1, **i32),
@@ -411,6 +469,16 @@ class PagedDecode:
                              scratch=torch.empty(nscratch, dtype=torch.uint8, device=self.device),
                              scratch_bytes=nscratch)
         return self._dev
+
+    def sparse_buffers(self, batch, bt_stride):
+        """Compacted block table [B * Hkv, bt_stride] and lengths [B * Hkv]."""
+        key = (batch, bt_stride)
+        if self._sparse is None or self._sparse["key"] != key:
+            i32 = dict(dtype=self.torch.int32, device=self.device)
+            n = batch * self.num_kv_heads
+            self._sparse = dict(key=key, bt=self.torch.empty((max(n, 1), bt_stride), **i32),
+                                sl=self.torch.empty(max(n, 1), **i32))
+        return self._sparse
 
     def plan_info(self):
         """Status, tile, item count and most items per worker of the last device plan
@@ -429,58 +497,87 @@ class PagedDecode:
 
     def __call__(self, q, k_cache, v_cache, block_table, seq_lens_h, scale, *, k_scale=None,
                  v_scale=None, seq_lens=None, out=None, lse_out=None, stream=None,
-                 partial_events=None):
-        """Run one decode step. ``seq_lens_h`` (host ints) drives the plan; ``seq_lens``
-        (device int32) defaults to the copy written next to the plan. ``partial_events``:
-        two torch.cuda.Events recorded around the decode_partial launch (for timing)."""
+                 partial_events=None, block_mask=None, block_mask_h=None):
+        """Run one decode step. ``seq_lens_h`` (host ints) drives a host plan; ``seq_lens``
+        (device int32) defaults to the copy written next to it and is required for a
+        device plan and for block-sparse steps. ``block_mask`` (device uint8 [B, Hkv,
+        mask_stride]) makes the step block-sparse; ``block_mask_h`` is its host copy, which
+        lets it be planned on the host (without it the plan is built on the device). ``partial_events``: two torch.cuda.Events recorded
+        around the decode_partial launch (for timing)."""
         if stream is not None:
             with self.torch.cuda.stream(stream):
                 return self(q, k_cache, v_cache, block_table, seq_lens_h, scale, k_scale=k_scale,
                             v_scale=v_scale, seq_lens=seq_lens, out=out, lse_out=lse_out,
-                            partial_events=partial_events)
+                            partial_events=partial_events, block_mask=block_mask,
+                            block_mask_h=block_mask_h)
         torch = self.torch
-        tile_dev = None
-        if self.device_plan:
+        Hkv, G = self.num_kv_heads, self.num_q_heads // self.num_kv_heads
+        B = int(seq_lens.shape[0]) if seq_lens is not None else len(seq_lens_h)
+        bt_stride = block_table.shape[1]
+        if block_mask is not None:
+            # The one-kv-head problem: B * Hkv requests over the cache viewed as
+            # [num_pages * Hkv, 1, P, D].
             if seq_lens is None or not getattr(seq_lens, "is_cuda", False):
+                raise ValueError("a block-sparse step needs seq_lens as a CUDA int32 tensor")
+            sp = self.sparse_buffers(B, bt_stride)
+            mask_stride = block_mask.shape[-1]
+            pkv_block_sparse_compact(block_table=block_table, seq_lens=seq_lens, block_mask=block_mask,
+                                     batch=B, num_kv_heads=Hkv, q_len=self.q_len,
+                                     page_size=self.page_size, bt_stride=bt_stride,
+                                     mask_stride=mask_stride, num_pages=k_cache.shape[0],
+                                     bt_out=sp["bt"], seq_lens_out=sp["sl"])
+            prob = dict(batch=B * Hkv, Hq=G, Hkv=1, split=Hkv, bt=sp["bt"], sl=sp["sl"],
+                        num_pages=k_cache.shape[0] * Hkv)
+            use_device_plan = self.device_plan or block_mask_h is None
+            if not use_device_plan:
+                lengths_h = pkv_block_sparse_lengths(seq_lens_h, block_mask_h, Hkv, self.q_len,
+                                                     self.page_size)
+        else:
+            prob = dict(batch=B, Hq=self.num_q_heads, Hkv=Hkv, split=1, bt=block_table, sl=seq_lens,
+                        num_pages=k_cache.shape[0])
+            lengths_h = seq_lens_h
+            use_device_plan = self.device_plan
+        tile_dev = None
+        if use_device_plan:
+            if prob["sl"] is None or not getattr(prob["sl"], "is_cuda", False):
                 raise ValueError("a device-built plan needs seq_lens as a CUDA int32 tensor")
-            B = int(seq_lens.shape[0])
-            d = self.device_buffers(B, block_table.shape[1])
-            pkv_plan_device(seq_lens=seq_lens, batch=B, q_len=self.q_len,
-                            num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
-                            head_dim=self.head_dim, page_size=self.page_size,
-                            kv_format=self.kv_format, tile_tokens=self.tile_tokens,
-                            num_workers=self.num_workers, max_items=d["cap"], items=d["items"],
-                            worker_offsets=d["offsets"], req_tile_base=d["rtb"], info=d["info"],
-                            scratch=d["scratch"], scratch_bytes=d["scratch_bytes"])
-            p = dict(T=self.tile_tokens, N=d["cap"], NP=d["cap"], W=self.num_workers, B=B, slot=None,
+            d = self.device_buffers(prob["batch"], bt_stride, prob["Hkv"])
+            pkv_plan_device(seq_lens=prob["sl"], batch=prob["batch"], q_len=self.q_len,
+                            num_q_heads=prob["Hq"], num_kv_heads=prob["Hkv"], head_dim=self.head_dim,
+                            page_size=self.page_size, kv_format=self.kv_format,
+                            tile_tokens=self.tile_tokens, num_workers=self.num_workers,
+                            max_items=d["cap"], items=d["items"], worker_offsets=d["offsets"],
+                            req_tile_base=d["rtb"], info=d["info"], scratch=d["scratch"],
+                            scratch_bytes=d["scratch_bytes"])
+            p = dict(T=self.tile_tokens, N=d["cap"], NP=d["cap"], W=self.num_workers, slot=None,
                      items=d["items"], worker_offsets=d["offsets"], req_tile_base=d["rtb"])
             tile_dev = d["info"][1:]
+            sl_dev = prob["sl"]
         else:
-            p = self.plan(seq_lens_h)
-            if seq_lens is None:
-                seq_lens = p["seq_lens"]
+            p = self.plan(lengths_h, prob["Hq"], prob["Hkv"])
+            sl_dev = prob["sl"] if prob["sl"] is not None else p["seq_lens"]
         ws, ws_bytes = self.workspace(p["NP"])
-        B = p["B"]
         if out is None:
             out = torch.empty((B, self.q_len, self.num_q_heads, self.head_dim), dtype=torch.bfloat16,
                               device=self.device)
         if partial_events is not None:
             partial_events[0].record()
-        pkv_decode_partial(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-                           seq_lens=seq_lens, items=p["items"], worker_offsets=p["worker_offsets"],
+        pkv_decode_partial(q=q, k_cache=k_cache, v_cache=v_cache, block_table=prob["bt"],
+                           seq_lens=sl_dev, items=p["items"], worker_offsets=p["worker_offsets"],
                            req_tile_base=p["req_tile_base"], workspace=ws, workspace_bytes=ws_bytes,
-                           num_items=p["N"], num_partials=p["NP"], num_pages=k_cache.shape[0], batch=B,
-                           q_len=self.q_len, num_q_heads=self.num_q_heads,
-                           num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
-                           page_size=self.page_size, bt_stride=block_table.shape[1],
+                           num_items=p["N"], num_partials=p["NP"], num_pages=prob["num_pages"],
+                           batch=prob["batch"], q_len=self.q_len, num_q_heads=prob["Hq"],
+                           num_kv_heads=prob["Hkv"], head_dim=self.head_dim,
+                           page_size=self.page_size, bt_stride=bt_stride,
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
-                           scale=scale, k_scale=k_scale, v_scale=v_scale, tile_tokens_dev=tile_dev)
+                           scale=scale, k_scale=k_scale, v_scale=v_scale, tile_tokens_dev=tile_dev,
+                           request_split=prob["split"])
         if partial_events is not None:
             partial_events[1].record()
-        pkv_combine(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
-                    req_tile_base=p["req_tile_base"], batch=B, q_len=self.q_len,
-                    num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
-                    head_dim=self.head_dim, out=out, lse_out=lse_out)
+        pkv_combine_split(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
+                          req_tile_base=p["req_tile_base"], batch=prob["batch"], q_len=self.q_len,
+                          num_q_heads=prob["Hq"], num_kv_heads=prob["Hkv"], head_dim=self.head_dim,
+                          request_split=prob["split"], out=out, lse_out=lse_out)
         k = p["slot"]
         if k is not None:
             if self._consumed[k] is None:

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstddef>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "kernels.hpp"
@@ -174,13 +175,20 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   constexpr size_t kV1Size = offsetof(pkv_decode_args, tile_tokens_dev);
   if (a->struct_size < kV1Size)
     return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size, kV1Size);
-  const int32_t* tile_dev = a->struct_size >= sizeof(pkv_decode_args) ? a->tile_tokens_dev : nullptr;
+  const bool has_tile_dev =
+      a->struct_size >= offsetof(pkv_decode_args, tile_tokens_dev) + sizeof(a->tile_tokens_dev);
+  const bool has_split =
+      a->struct_size >= offsetof(pkv_decode_args, request_split) + sizeof(a->request_split);
+  const int32_t* tile_dev = has_tile_dev ? a->tile_tokens_dev : nullptr;
+  const int split = (has_split && a->request_split != 0) ? a->request_split : 1;
   int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
                        a->kv_format);
   if (st != PKV_OK) return st;
   if (a->batch < 0 || a->num_items < 0 || a->num_partials < a->num_items || a->num_pages < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative size or num_partials < num_items");
   if (a->num_workers < 1) return fail(PKV_ERR_INVALID_ARG, "num_workers %d < 1", a->num_workers);
+  if (split < 1 || a->batch % split != 0)
+    return fail(PKV_ERR_INVALID_ARG, "request_split %d does not divide batch %d", split, a->batch);
   const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
   const int64_t quantum = pkv::tile_quantum(a->page_size, fp8);
   if (tile_dev == nullptr && (a->tile_tokens < 1 || a->tile_tokens % quantum != 0))
@@ -235,6 +243,7 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   p.bt_stride = a->bt_stride;
   p.tile_tokens = a->tile_tokens;
   p.tile_tokens_dev = tile_dev;
+  p.request_split = split;
   p.qk_scale_log2 = a->scale * kLog2e;
   const hipError_t e = pkv::launch_decode_partial(p, a->head_dim, fp8, a->num_workers,
                                                   static_cast<hipStream_t>(stream));
@@ -348,6 +357,76 @@ int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_hea
   return PKV_OK;
 }
 
+int pkv_block_sparse_compact(const int32_t* block_table, const int32_t* seq_lens,
+                             const uint8_t* block_mask, int batch, int num_kv_heads,
+                             int q_len, int page_size, int bt_stride, int mask_stride,
+                             int64_t num_pages, int32_t* bt_out, int32_t* seq_lens_out,
+                             void* stream) {
+  if (batch < 0 || num_kv_heads < 1 || q_len < 1 || page_size < 1 || bt_stride < 1 ||
+      mask_stride < bt_stride || num_pages < 0)
+    return fail(PKV_ERR_INVALID_ARG, "sizes out of range (batch %d, kv heads %d, q_len %d, P %d, "
+                "bt_stride %d, mask_stride %d)", batch, num_kv_heads, q_len, page_size, bt_stride,
+                mask_stride);
+  if (num_pages * num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "num_pages x num_kv_heads = %lld does not fit int32",
+                static_cast<long long>(num_pages * num_kv_heads));
+  if (batch == 0) return PKV_OK;
+  if (!block_table || !seq_lens || !block_mask || !bt_out || !seq_lens_out)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(bt_out, 4) ||
+      !aligned(seq_lens_out, 4))
+    return fail(PKV_ERR_ALIGNMENT, "int32 arrays must be 4-byte aligned");
+  pkv::BlockSparseParams p;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.block_mask = block_mask;
+  p.bt_out = bt_out;
+  p.seq_lens_out = seq_lens_out;
+  p.batch = batch;
+  p.num_kv_heads = num_kv_heads;
+  p.q_len = q_len;
+  p.page_size = page_size;
+  p.bt_stride = bt_stride;
+  p.mask_stride = mask_stride;
+  const hipError_t e = pkv::launch_block_sparse_compact(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "block_sparse_compact launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_block_sparse_lengths(int batch, const int32_t* seq_lens_h, const uint8_t* block_mask_h,
+                             int num_kv_heads, int q_len, int page_size, int mask_stride,
+                             int32_t* lengths_out_h) {
+  if (batch < 0 || num_kv_heads < 1 || q_len < 1 || page_size < 1 || mask_stride < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes out of range");
+  if (batch > 0 && (!seq_lens_h || !block_mask_h || !lengths_out_h))
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  const int st = check_seq_lens(batch, seq_lens_h, q_len);
+  if (st != PKV_OK) return st;
+  for (int b = 0; b < batch; ++b) {
+    const int L = seq_lens_h[b];
+    const int n = static_cast<int>(pkv::ceil_div(L, page_size));
+    if (n > mask_stride)
+      return fail(PKV_ERR_INVALID_ARG, "request %d has %d pages, mask_stride is %d", b, n,
+                  mask_stride);
+    const int first_query_page = (L - q_len) / page_size;
+    for (int g = 0; g < num_kv_heads; ++g) {
+      const uint8_t* m = block_mask_h + (static_cast<int64_t>(b) * num_kv_heads + g) * mask_stride;
+      // Nonzero bytes among the pages before the query pages, eight at a time: a
+      // byte's high bit of ((x & 0x7f..) + 0x7f..) | x is set iff the byte is nonzero.
+      int attended = 0, pg = 0;
+      for (; pg + 8 <= first_query_page; pg += 8) {
+        uint64_t x;
+        std::memcpy(&x, m + pg, 8);
+        const uint64_t lo7 = 0x7f7f7f7f7f7f7f7fULL;
+        attended += __builtin_popcountll((((x & lo7) + lo7) | x) & ~lo7);
+      }
+      for (; pg < first_query_page; ++pg) attended += (m[pg] != 0);
+      lengths_out_h[b * num_kv_heads + g] = L - (first_query_page - attended) * page_size;
+    }
+  }
+  return PKV_OK;
+}
+
 static_assert(pkv::PKV_DEV_OK == PKV_OK && pkv::PKV_DEV_ERR_SEQ == PKV_ERR_SEQ &&
                   pkv::PKV_DEV_ERR_UNSUPPORTED == PKV_ERR_UNSUPPORTED &&
                   pkv::PKV_DEV_ERR_WORKSPACE == PKV_ERR_WORKSPACE,
@@ -358,11 +437,22 @@ static_assert(8 * pkv::kMaxDevicePlanCandidates + 4 * pkv::kMaxDevicePlanCandida
 int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_partials,
                 const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
                 int num_kv_heads, int head_dim, void* out, float* lse_out, void* stream) {
+  return pkv_combine_split(workspace, workspace_bytes, num_partials, req_tile_base, batch, q_len,
+                           num_q_heads, num_kv_heads, head_dim, 1, out, lse_out, stream);
+}
+
+int pkv_combine_split(const void* workspace, size_t workspace_bytes, int64_t num_partials,
+                      const int32_t* req_tile_base, int batch, int q_len, int num_q_heads,
+                      int num_kv_heads, int head_dim, int request_split, void* out,
+                      float* lse_out, void* stream) {
   const int st = check_shape(q_len, num_q_heads, num_kv_heads, head_dim, 16, PKV_KV_BF16);
   if (st != PKV_OK) return st;
   if (batch < 0 || num_partials < 0)
     return fail(PKV_ERR_INVALID_ARG, "batch %d / num_partials %lld negative", batch,
                 static_cast<long long>(num_partials));
+  if (request_split < 1 || batch % request_split != 0)
+    return fail(PKV_ERR_INVALID_ARG, "request_split %d does not divide batch %d", request_split,
+                batch);
   if (batch == 0) return PKV_OK;
   if (static_cast<int64_t>(batch) * q_len * num_q_heads > INT32_MAX / 64)
     return fail(PKV_ERR_UNSUPPORTED, "too many output rows");
@@ -389,6 +479,7 @@ int pkv_combine(const void* workspace, size_t workspace_bytes, int64_t num_parti
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.rows = rows;
+  p.request_split = request_split;
   const hipError_t e = pkv::launch_combine(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   return PKV_OK;

@@ -98,7 +98,14 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
   }
   den = wave_sum(den);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* orow = p.out + static_cast<int64_t>(row) * D;
+  // out is [B / split, Tq, split * Hq, D] (and lse_out likewise without D); with
+  // split 1 the row index is the output row.
+  int64_t orow_idx = row;
+  if (p.request_split != 1) {
+    const int qb = b / p.request_split, part = b - qb * p.request_split;
+    orow_idx = ((static_cast<int64_t>(qb) * p.q_len + t) * p.request_split + part) * p.num_q_heads + h;
+  }
+  uint16_t* orow = p.out + orow_idx * D;
   if constexpr (E == 2) {
     f32x2 v = {acc[0] * inv, acc[1] * inv};
     *reinterpret_cast<bf16x2*>(orow + 2 * lane) = __builtin_convertvector(v, bf16x2);
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
     orow[lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[0] * inv));
   }
   if (p.lse_out != nullptr && lane == 0)
-    p.lse_out[row] = den > 0.f ? (m_use + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+    p.lse_out[orow_idx] = den > 0.f ? (m_use + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -299,6 +299,7 @@ __device__ __forceinline__ void process_chunk(u32x4 (&kop)[2][D / 32], u32x4 (&v
 // Scalar shape arguments of the decode kernel.
 struct DecodeShape {
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
+  int request_split;  // work-list request b is part b % split of the caller's request b / split
   float qk_scale_log2;
 };
 
@@ -401,8 +402,12 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       if (n < M) {
         const int t = n / G;
         const int head = u_info.g * G + (n - t * G);
+        // q is [B / split, Tq, split * Hq, D]; with split 1 this is [B, Tq, Hq, D].
+        const int split = sh.request_split;
+        const int64_t qb = (split == 1) ? u_info.b : u_info.b / split;
+        const int part = (split == 1) ? 0 : u_info.b - static_cast<int>(qb) * split;
         const uint16_t* qrow =
-            q + ((static_cast<int64_t>(u_info.b) * Tq + t) * sh.num_q_heads + head) * D;
+            q + (((qb * Tq + t) * split + part) * sh.num_q_heads + head) * D;
 #pragma unroll
         for (int s = 0; s < C::kSteps; ++s)
           qf_next[s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
@@ -513,8 +518,9 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
 hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8, int num_workers,
                                  hipStream_t stream) {
   const dim3 grid(num_workers), block(kThreads);
-  const DecodeShape sh = {p.q_len, p.num_q_heads, p.num_kv_heads, p.group, p.rows,
-                          p.page_size, p.bt_stride, p.tile_tokens, p.qk_scale_log2};
+  const DecodeShape sh = {p.q_len,     p.num_q_heads, p.num_kv_heads, p.group,
+                          p.rows,      p.page_size,   p.bt_stride,    p.tile_tokens,
+                          p.request_split, p.qk_scale_log2};
 #define PKV_LAUNCH(DIM, F8)                                                                   \
   hipLaunchKernelGGL((decode_partial_kernel<DIM, F8>), grid, block, 0, stream, p.q, p.k_cache, \
                      p.v_cache, p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items,     \

@@ -28,6 +28,7 @@ struct DecodeParams {
   float* ws_lse;              // [num_partials, M]
   const int32_t* tile_tokens_dev;  // if set, T is read from here instead of tile_tokens
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
+  int request_split;          // work-list request b = part b % split of request b / split
   float qk_scale_log2;        // softmax scale * log2(e)
 };
 
@@ -38,7 +39,19 @@ struct CombineParams {
   uint16_t* out;                 // bf16 [B, Tq, Hq, D]
   float* lse_out;                // [B, Tq, Hq] or null
   int batch, q_len, num_q_heads, num_kv_heads, group, rows;
+  int request_split;             // as in DecodeParams
 };
+
+struct BlockSparseParams {
+  const int32_t* block_table;    // [B, bt_stride]
+  const int32_t* seq_lens;       // [B]
+  const uint8_t* block_mask;     // [B, Hkv, mask_stride]
+  int32_t* bt_out;               // [B * Hkv, bt_stride]: phys * Hkv + g of attended pages
+  int32_t* seq_lens_out;         // [B * Hkv]
+  int batch, num_kv_heads, q_len, page_size, bt_stride, mask_stride;
+};
+
+hipError_t launch_block_sparse_compact(const BlockSparseParams& p, hipStream_t stream);
 
 // Device planner limits: one thread per worker, the requests sorted in LDS.
 constexpr int kMaxDevicePlanWorkers = 1024;

@@ -69,6 +69,8 @@ class WorkerTree {
 struct Scratch {
   std::vector<int64_t> loads, counts, full, sorted;
   std::vector<int32_t> reqs, nfull, rem;  // per request: full tiles, last-tile tokens
+  std::vector<int32_t> tmp;               // radix-sort buffer
+  std::vector<uint32_t> keys, tmp_keys;
   WorkerTree heap;
 };
 
@@ -87,13 +89,37 @@ int64_t split_requests(int batch, const int32_t* seq_lens, int64_t T, Scratch& s
   return f;
 }
 
+// The requests with a partial tile, longest partial tile first, ties by request
+// index: a least-significant-digit radix sort (stable) of INT32_MAX - rem over the
+// requests in index order, skipping the 8-bit digits on which all keys agree.
 void partial_requests(int batch, Scratch& s) {
   s.reqs.clear();
+  s.keys.clear();
+  uint32_t all_or = 0, all_and = UINT32_MAX;
   for (int b = 0; b < batch; ++b)
-    if (s.rem[b] != 0) s.reqs.push_back(b);
-  const int32_t* rem = s.rem.data();
-  std::stable_sort(s.reqs.begin(), s.reqs.end(),
-                   [rem](int32_t x, int32_t y) { return rem[x] > rem[y]; });
+    if (s.rem[b] != 0) {
+      const uint32_t key = static_cast<uint32_t>(INT32_MAX - s.rem[b]);
+      s.reqs.push_back(b);
+      s.keys.push_back(key);
+      all_or |= key;
+      all_and &= key;
+    }
+  const size_t n = s.reqs.size();
+  s.tmp.resize(n);
+  s.tmp_keys.resize(n);
+  for (int shift = 0; shift < 32; shift += 8) {
+    if ((((all_or ^ all_and) >> shift) & 0xFF) == 0) continue;  // digit constant
+    size_t count[257] = {0};
+    for (size_t i = 0; i < n; ++i) ++count[((s.keys[i] >> shift) & 0xFF) + 1];
+    for (int d = 0; d < 256; ++d) count[d + 1] += count[d];
+    for (size_t i = 0; i < n; ++i) {
+      const size_t pos = count[(s.keys[i] >> shift) & 0xFF]++;
+      s.tmp[pos] = s.reqs[i];
+      s.tmp_keys[pos] = s.keys[i];
+    }
+    s.reqs.swap(s.tmp);
+    s.keys.swap(s.tmp_keys);
+  }
 }
 
 // Streaming time of the per-worker loads in chip-token units (see kWorkerRatio):

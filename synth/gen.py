@@ -221,10 +221,12 @@ def attended_pages(inp, block_mask):
     return out
 
 
-def sparse_algorithmic_bytes(inp, block_mask):
+def sparse_algorithmic_bytes(inp, block_mask, decode_only=False):
     """Bytes a block-sparse decode step must move at minimum: K and V of the
     attended tokens, Q, the bf16 output, the mask entries and block-table entries of
-    every page, seq_lens and (fp8) the scales of attended pages."""
+    every page, seq_lens and (fp8) the scales of attended pages. ``decode_only``: the
+    share of the split-KV partial kernel - attended K/V, Q, one compacted block-table
+    entry per attended page, the compacted lengths and the attended pages' scales."""
     eb = 2 if inp.kv_format == "bf16" else 1
     P = inp.page_size
     tokens = pages_att = pages_all = 0
@@ -238,6 +240,8 @@ def sparse_algorithmic_bytes(inp, block_mask):
     kv = tokens * inp.head_dim * eb * 2
     q = inp.batch * inp.q_len * inp.num_q_heads * inp.head_dim * 2
     scales = 0 if inp.kv_format == "bf16" else 2 * 4 * pages_att
+    if decode_only:
+        return kv + q + 4 * pages_att + 4 * inp.batch * inp.num_kv_heads + scales
     return kv + 2 * q + 4 * pages_all + pages_all * inp.num_kv_heads + 4 * inp.batch + scales
 
 

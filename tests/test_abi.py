@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -269,6 +269,58 @@ def test_plan_device_argument_errors(kw, status):
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_plan_device(**plan_device_kwargs(**kw))
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("fmt,P,q_len", [("bf16", 16, 1), ("bf16", 32, 4), ("fp8", 64, 2)])
+def test_block_sparse_lengths_match_the_attended_pages(fmt, P, q_len):
+    c = dict(name="s", batch=6, seq_lens=(4, 15, 16, 17, 100, 700), q_len=q_len, num_q_heads=8,
+             num_kv_heads=2, head_dim=64, page_size=P, kv_format=fmt)
+    inp = synth.make_inputs(c, seed=1)
+    for keep in (0.0, 0.3, 1.0):
+        mask = synth.make_block_mask(inp, keep, seed=2)
+        got = pkv.pkv_block_sparse_lengths(inp.seq_lens, mask, 2, q_len, P)
+        att = synth.attended_pages(inp, mask)
+        want = [sum(min(P, int(inp.seq_lens[b]) - p * P) for p in att[b][g])
+                for b in range(inp.batch) for g in range(2)]
+        assert got.tolist() == want
+
+
+def test_block_sparse_lengths_errors():
+    m = np.ones((2, 1, 4), np.uint8)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_block_sparse_lengths([5, 0], m, 1, 1, 16)
+    assert e.value.status == pkv.PKV_ERR_SEQ
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_block_sparse_lengths([5, 65], m, 1, 1, 16)      # 5 pages, mask rows of 4
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(mask_stride=3), pkv.PKV_ERR_INVALID_ARG),              # shorter than bt_stride
+    (dict(num_pages=1 << 29), pkv.PKV_ERR_UNSUPPORTED),           # x 8 kv heads > int32
+    (dict(block_mask=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(bt_out=7 * A + 2), pkv.PKV_ERR_ALIGNMENT),
+])
+def test_block_sparse_compact_errors(kw, status):
+    base = dict(block_table=A, seq_lens=2 * A, block_mask=3 * A, batch=2, num_kv_heads=8, q_len=1,
+                page_size=16, bt_stride=4, mask_stride=4, num_pages=64, bt_out=7 * A,
+                seq_lens_out=8 * A, stream=0)
+    base.update(kw)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_block_sparse_compact(**base)
+    assert e.value.status == status
+
+
+def test_request_split_must_divide_the_batch():
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode_partial(**decode_kwargs(request_split=3))
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_combine_split(workspace=9 * A, workspace_bytes=1 << 30, num_partials=4,
+                              req_tile_base=8 * A, batch=6, q_len=1, num_q_heads=4, num_kv_heads=1,
+                              head_dim=128, request_split=4, out=A, stream=0)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,status", [

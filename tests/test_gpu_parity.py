@@ -54,8 +54,8 @@ def excess(out, ref, tol):
     return float(np.max(err - np.maximum(tol, 0.6 * bf16_ulp(ref)), initial=-np.inf))
 
 
-def check(inp, out, lse, pairs=None, tag=""):
-    ref_out, ref_lse = oracle.decode_attention(inp, pairs=pairs)
+def check(inp, out, lse, pairs=None, tag="", block_mask=None):
+    ref_out, ref_lse = oracle.decode_attention(inp, pairs=pairs, block_mask=block_mask)
     if pairs is not None:
         sel = np.zeros(ref_lse.shape, dtype=bool)
         G = inp.num_q_heads // inp.num_kv_heads
