@@ -88,6 +88,10 @@ def main():
     ap.add_argument("--block-sparse", type=float, default=None, metavar="KEEP",
                     help="block-sparse decode: each (request, kv head, page) attended with "
                          "probability KEEP (seeded), plus the pages of the query tokens")
+    ap.add_argument("--append", action="store_true",
+                    help="start every step with the fused KV append (rotary embedding of q "
+                         "and the new k rows, paged write, fp8 quantise-on-write) of the "
+                         "batch's newest tokens")
     ap.add_argument("--device-plan", action="store_true",
                     help="build the plan on the GPU (pkv_plan_device) from device seq_lens "
                          "instead of on the host")
@@ -132,6 +136,14 @@ def main():
         vs = torch.from_numpy(inp.v_scale).to(dev)
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl_dev = torch.from_numpy(inp.seq_lens).to(dev)
+    if args.append:
+        algo += synth.append_algorithmic_bytes(inp)
+        kn_h, vn_h, _ = synth.new_token_rows(inp, seed=2)
+        as_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        k_new, v_new = as_bf16(kn_h), as_bf16(vn_h)
+        cos_h, sin_h = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+        rope_cos, rope_sin = torch.from_numpy(cos_h).to(dev), torch.from_numpy(sin_h).to(dev)
+        q_rot = torch.empty_like(q)
     if mask_h is not None:
         mask_d = torch.from_numpy(mask_h).to(dev)
     seq_lens_h = inp.seq_lens.copy()
@@ -144,7 +156,12 @@ def main():
                       device=dev)
 
     def step(events=None):
-        runner(q, k, v, bt, seq_lens_h, inp.scale, k_scale=ks, v_scale=vs, seq_lens=sl_dev,
+        q_step = q
+        if args.append:
+            runner.append(k_new, v_new, k, v, bt, sl_dev, q=q, q_out=q_rot, rope_cos=rope_cos,
+                          rope_sin=rope_sin, k_scale=ks, v_scale=vs)
+            q_step = q_rot
+        runner(q_step, k, v, bt, seq_lens_h, inp.scale, k_scale=ks, v_scale=vs, seq_lens=sl_dev,
                out=out, partial_events=events, block_mask=mask_d, block_mask_h=mask_h)
 
     log("warmup %d steps" % args.warmup)
@@ -162,6 +179,9 @@ def main():
         step_desc = "host plan (read in place by the kernels) + decode_partial + combine"
     if mask_h is not None:
         step_desc = "block mask compaction + " + step_desc
+    if args.append:
+        step_desc = "fused KV append (rotary, paged write%s) + " % (
+            ", fp8 quantise-on-write" if inp.kv_format != "bf16" else "") + step_desc
     log("plan: tile %d tokens, %d items, %d workers" % (plan["T"], plan["N"], plan["W"]))
 
     K = args.steps

@@ -286,6 +286,51 @@ int pkv_block_sparse_lengths(int batch, const int32_t* seq_lens_h, const uint8_t
                              int num_kv_heads, int q_len, int page_size, int mask_stride,
                              int32_t* lengths_out_h);
 
+/* Arguments of pkv_kv_append (all pointers device memory, caller-owned). */
+typedef struct pkv_kv_append_args {
+  size_t struct_size;             /* sizeof(pkv_kv_append_args) */
+  const void* k_new;              /* bf16 [B, Tq, Hkv, D]: the step's new keys */
+  const void* v_new;              /* bf16 [B, Tq, Hkv, D]: the step's new values */
+  const void* q;                  /* bf16 [B, Tq, Hq, D] or NULL */
+  void* q_out;                    /* bf16 [B, Tq, Hq, D]: rotated q (may equal q), or NULL */
+  const float* rope_cos;          /* fp32 [max_pos, D/2] or NULL: no rotary embedding */
+  const float* rope_sin;          /* fp32 [max_pos, D/2]; NULL iff rope_cos is */
+  void* k_cache;                  /* [num_pages, Hkv, P, D], bf16 or e4m3fn, written */
+  void* v_cache;
+  float* k_scale;                 /* fp32 [num_pages, Hkv]; NULL iff bf16; read and written */
+  float* v_scale;
+  const int32_t* block_table;     /* int32 [B, bt_stride] */
+  const int32_t* seq_lens;        /* int32 [B]; L_b counts the Tq new tokens */
+  int64_t num_pages;
+  int batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride;
+  int kv_format;                  /* enum pkv_kv_format */
+  int max_pos;                    /* rows of the rotation tables; >= bt_stride * P */
+} pkv_kv_append_args;
+
+/*
+ * Fused KV append: the step before decode attention (the HALOps README's fused
+ * pre-processing of paged-KV decode; per-tile FP8 scaling as in the HALOps review),
+ * in one kernel. Request b's Tq new tokens sit at positions L_b - Tq .. L_b - 1.
+ * - Rotary embedding (when rope_cos is set), half-split form: for i < D/2, with
+ *   c = rope_cos[pos, i], s = rope_sin[pos, i], x1 = x[i], x2 = x[i + D/2]:
+ *   x[i] = x1*c - x2*s and x[i + D/2] = x2*c + x1*s, each product, sum and difference
+ *   one IEEE float32 rounding; applied to the new k rows and, when q_out is set, to
+ *   q (all heads) into q_out, rounded to bf16 (nearest even).
+ * - bf16 cache: the (rotated) k rows and the v rows are stored at their positions
+ *   (bit copies without rotation).
+ * - fp8 cache: per page and kv head touched, K and V apart, with a = the largest
+ *   |value| among the page's new rows: if the new rows start at the page's first
+ *   slot the scale becomes a / 448 (1 if a == 0); else the page keeps its scale s
+ *   while a / s <= 448, and otherwise takes a / 448 and re-encodes its earlier codes
+ *   from their values code * s. Codes: nearest e4m3fn value (ties to the even code),
+ *   saturating at +-448, sign kept. Divisions and products are IEEE float32.
+ * Pages are written in place; a page must belong to one request. Enqueue only.
+ * Errors: INVALID_ARG (null pointer, sizes, scales given iff fp8, one table only,
+ * max_pos < bt_stride * P), UNSUPPORTED (shape rules), ALIGNMENT (16-byte rows and
+ * caches, 4-byte tables), HIP.
+ */
+int pkv_kv_append(const pkv_kv_append_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class KvAppendArgs(ctypes.Structure):
+    """Mirror of ``pkv_kv_append_args`` (include/pkv.h)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("q_out", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("batch", ctypes.c_int), ("q_len", ctypes.c_int), ("num_q_heads", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("max_pos", ctypes.c_int),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libpkv.so is not built (expected at %s); run "
@@ -104,6 +121,7 @@ def _load():
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
         "pkv_block_sparse_lengths": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_void_p, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]),
+        "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(KvAppendArgs), ctypes.c_void_p]),
         "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -311,6 +329,27 @@ def pkv_block_sparse_lengths(seq_lens_h, block_mask_h, num_kv_heads, q_len, page
     return out
 
 
+def pkv_kv_append(*, k_new, v_new, k_cache, v_cache, block_table, seq_lens, num_pages, batch,
+                  q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride, kv_format,
+                  q=None, q_out=None, rope_cos=None, rope_sin=None, max_pos=0, k_scale=None,
+                  v_scale=None, stream=None):
+    """Enqueue the fused KV append (rotary embedding, paged write, fp8 quantise-on-write)."""
+    a = KvAppendArgs()
+    a.struct_size = ctypes.sizeof(KvAppendArgs)
+    a.k_new, a.v_new = _ptr(k_new, "k_new"), _ptr(v_new, "v_new")
+    a.q, a.q_out = _ptr(q, "q"), _ptr(q_out, "q_out")
+    a.rope_cos, a.rope_sin = _ptr(rope_cos, "rope_cos"), _ptr(rope_sin, "rope_sin")
+    a.k_cache, a.v_cache = _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
+    a.k_scale, a.v_scale = _ptr(k_scale, "k_scale"), _ptr(v_scale, "v_scale")
+    a.block_table, a.seq_lens = _ptr(block_table, "block_table"), _ptr(seq_lens, "seq_lens")
+    a.num_pages, a.batch, a.q_len = num_pages, batch, q_len
+    a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
+    a.page_size, a.bt_stride = page_size, bt_stride
+    a.kv_format = KV_FORMATS.get(kv_format, kv_format)
+    a.max_pos = max_pos
+    _check(_lib.pkv_kv_append(ctypes.byref(a), _stream_handle(stream)), "pkv_kv_append")
+
+
 # ---------------------------------------------------------------------------------
 # Per-step runner
 
@@ -487,6 +526,20 @@ class PagedDecode:
             return None
         st, T, N, mx = (int(x) for x in self._dev["info"].cpu())
         return dict(status=st, T=T, N=N, max_items_per_worker=mx, capacity=self._dev["cap"])
+
+    def append(self, k_new, v_new, k_cache, v_cache, block_table, seq_lens, *, q=None, q_out=None,
+               rope_cos=None, rope_sin=None, k_scale=None, v_scale=None, stream=None):
+        """Enqueue the fused KV append for this runner's shapes: the step's new k/v rows
+        (bf16 [B, Tq, Hkv, D]) into the paged cache, optionally rotating q into q_out and
+        the k rows by the tables (fp32 [max_pos, D/2]); fp8 pages are quantised on write."""
+        pkv_kv_append(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                      block_table=block_table, seq_lens=seq_lens, num_pages=k_cache.shape[0],
+                      batch=int(seq_lens.shape[0]), q_len=self.q_len, num_q_heads=self.num_q_heads,
+                      num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
+                      page_size=self.page_size, bt_stride=block_table.shape[1],
+                      kv_format=self.kv_format, q=q, q_out=q_out, rope_cos=rope_cos,
+                      rope_sin=rope_sin, max_pos=0 if rope_cos is None else rope_cos.shape[0],
+                      k_scale=k_scale, v_scale=v_scale, stream=stream)
 
     def workspace(self, num_partials):
         nbytes = pkv_workspace_bytes(max(num_partials, 1), self.rows, self.head_dim)

@@ -427,6 +427,62 @@ int pkv_block_sparse_lengths(int batch, const int32_t* seq_lens_h, const uint8_t
   return PKV_OK;
 }
 
+int pkv_kv_append(const pkv_kv_append_args* a, void* stream) {
+  if (a == nullptr) return fail(PKV_ERR_INVALID_ARG, "null args");
+  if (a->struct_size < sizeof(pkv_kv_append_args))
+    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size,
+                sizeof(pkv_kv_append_args));
+  int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
+                       a->kv_format);
+  if (st != PKV_OK) return st;
+  if (a->batch < 0 || a->num_pages < 0 || a->bt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes out of range (batch %d, pages %lld, bt_stride %d)",
+                a->batch, static_cast<long long>(a->num_pages), a->bt_stride);
+  if (a->batch == 0) return PKV_OK;
+  const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
+  if (!a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (fp8 != (a->k_scale != nullptr) || fp8 != (a->v_scale != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale must be given exactly for fp8 KV");
+  if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "rope_cos and rope_sin go together");
+  if ((a->q == nullptr) != (a->q_out == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q and q_out go together");
+  if (a->rope_cos != nullptr &&
+      static_cast<int64_t>(a->max_pos) < static_cast<int64_t>(a->bt_stride) * a->page_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_pos %d < bt_stride x page_size", a->max_pos);
+  if (!aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->k_cache, 16) ||
+      !aligned(a->v_cache, 16) || (a->q && (!aligned(a->q, 16) || !aligned(a->q_out, 16))) ||
+      !aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) ||
+      (a->rope_cos && (!aligned(a->rope_cos, 4) || !aligned(a->rope_sin, 4))) ||
+      (fp8 && (!aligned(a->k_scale, 4) || !aligned(a->v_scale, 4))))
+    return fail(PKV_ERR_ALIGNMENT, "rows and caches need 16 bytes, tables 4");
+  pkv::KvAppendParams p;
+  p.k_new = static_cast<const uint16_t*>(a->k_new);
+  p.v_new = static_cast<const uint16_t*>(a->v_new);
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_out = static_cast<uint16_t*>(a->q_out);
+  p.rope_cos = a->rope_cos;
+  p.rope_sin = a->rope_sin;
+  p.k_cache = static_cast<uint8_t*>(a->k_cache);
+  p.v_cache = static_cast<uint8_t*>(a->v_cache);
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.page_size = a->page_size;
+  p.bt_stride = a->bt_stride;
+  p.fp8 = fp8;
+  const hipError_t e = pkv::launch_kv_append(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 static_assert(pkv::PKV_DEV_OK == PKV_OK && pkv::PKV_DEV_ERR_SEQ == PKV_ERR_SEQ &&
                   pkv::PKV_DEV_ERR_UNSUPPORTED == PKV_ERR_UNSUPPORTED &&
                   pkv::PKV_DEV_ERR_WORKSPACE == PKV_ERR_WORKSPACE,

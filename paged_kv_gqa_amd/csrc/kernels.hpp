@@ -53,6 +53,28 @@ struct BlockSparseParams {
 
 hipError_t launch_block_sparse_compact(const BlockSparseParams& p, hipStream_t stream);
 
+// Largest head dimension of any kernel.
+constexpr int kMaxHeadDim = 128;
+
+struct KvAppendParams {
+  const uint16_t* k_new;         // bf16 [B, Tq, Hkv, D]
+  const uint16_t* v_new;
+  const uint16_t* q;             // bf16 [B, Tq, Hq, D], rotated into q_out (may alias)
+  uint16_t* q_out;               // or null
+  const float* rope_cos;         // [max_pos, D/2] or null (no rotation)
+  const float* rope_sin;
+  uint8_t* k_cache;              // [num_pages, Hkv, P, D] bf16 or e4m3fn
+  uint8_t* v_cache;
+  float* k_scale;                // [num_pages, Hkv] (fp8)
+  float* v_scale;
+  const int32_t* block_table;    // [B, bt_stride]
+  const int32_t* seq_lens;       // [B], counting the new tokens
+  int batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride;
+  bool fp8;
+};
+
+hipError_t launch_kv_append(const KvAppendParams& p, hipStream_t stream);
+
 // Device planner limits: one thread per worker, the requests sorted in LDS.
 constexpr int kMaxDevicePlanWorkers = 1024;
 constexpr int kMaxDevicePlanBatch = 4096;

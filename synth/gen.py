@@ -198,6 +198,44 @@ def apply_poison(inp):
     return inp
 
 
+def rope_tables(max_pos, head_dim, base=10000.0):
+    """Rotary-embedding tables: cos and sin of pos * base^(-2i/D), i < D/2, computed
+    in float64 and stored as float32 [max_pos, D/2] (inputs of the append)."""
+    inv = base ** (-np.arange(head_dim // 2, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def new_token_rows(inp, seed=0, scale=1.0):
+    """The step's new k and v rows (bf16 bits [B, Tq, Hkv, D]) and a new q (bf16 bits
+    [B, Tq, Hq, D]), standard normal times ``scale`` (a scalar or a [B, Hkv] array)."""
+    rng = np.random.default_rng(seed)
+    B, Tq, Hkv, D = inp.batch, inp.q_len, inp.num_kv_heads, inp.head_dim
+    sc = np.broadcast_to(np.asarray(scale, np.float32), (B, Hkv))[:, None, :, None]
+    k = f32_to_bf16_bits((rng.standard_normal((B, Tq, Hkv, D), dtype=np.float32) * sc).astype(np.float32))
+    v = f32_to_bf16_bits((rng.standard_normal((B, Tq, Hkv, D), dtype=np.float32) * sc).astype(np.float32))
+    q = f32_to_bf16_bits(rng.standard_normal((B, Tq, inp.num_q_heads, D), dtype=np.float32))
+    return k, v, q
+
+
+def append_algorithmic_bytes(inp, rope=True):
+    """Bytes the fused append must move at minimum: the new k and v rows read (bf16)
+    and written to the cache, q read and written rotated, the rotation table rows of
+    the new positions, the block-table entries of the touched pages, seq_lens and
+    (fp8) the touched pages' scales read and written."""
+    eb = 2 if inp.kv_format == "bf16" else 1
+    B, Tq, Hkv, Hq, D, P = (inp.batch, inp.q_len, inp.num_kv_heads, inp.num_q_heads,
+                            inp.head_dim, inp.page_size)
+    rows = B * Tq * Hkv * D
+    touched = sum((int(L) - 1) // P - (int(L) - Tq) // P + 1 for L in inp.seq_lens)
+    total = 2 * rows * 2 + 2 * rows * eb + 4 * touched + 4 * B
+    if rope:
+        total += 2 * B * Tq * Hq * D * 2 + 2 * B * Tq * (D // 2) * 4
+    if inp.kv_format != "bf16":
+        total += 2 * 2 * 4 * touched * Hkv
+    return total
+
+
 def make_block_mask(inp, keep, seed=1):
     """Block mask for block-sparse decode: uint8 [B, Hkv, bt_stride], 1 = page
     attended, each (request, kv head, logical page) kept with probability ``keep``

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -321,6 +321,36 @@ def test_request_split_must_divide_the_batch():
                               req_tile_base=8 * A, batch=6, q_len=1, num_q_heads=4, num_kv_heads=1,
                               head_dim=128, request_split=4, out=A, stream=0)
     assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+
+
+def append_kwargs(**kw):
+    base = dict(k_new=A, v_new=2 * A, k_cache=3 * A, v_cache=4 * A, block_table=5 * A,
+                seq_lens=6 * A, num_pages=8, batch=2, q_len=1, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, page_size=16, bt_stride=4, kv_format="bf16", stream=0)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kv_format="fp8", page_size=64), pkv.PKV_ERR_INVALID_ARG),              # no scales
+    (dict(k_scale=7 * A), pkv.PKV_ERR_INVALID_ARG),                               # bf16 with scales
+    (dict(rope_cos=7 * A), pkv.PKV_ERR_INVALID_ARG),                              # one table only
+    (dict(q=7 * A), pkv.PKV_ERR_INVALID_ARG),                                     # q without q_out
+    (dict(rope_cos=7 * A, rope_sin=8 * A, max_pos=63), pkv.PKV_ERR_INVALID_ARG),  # < 4 x 16
+    (dict(k_new=A + 4), pkv.PKV_ERR_ALIGNMENT),
+    (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(q_len=5), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bt_stride=0), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_kv_append_argument_errors(kw, status):
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_kv_append(**append_kwargs(**kw))
+    assert e.value.status == status
+
+
+def test_kv_append_empty_batch_is_a_no_op():
+    pkv.pkv_kv_append(**append_kwargs(batch=0))
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -1,0 +1,171 @@
+"""Fused KV append on an MI355X against the oracle, bit for bit: the whole cache and
+scales after the append (bf16 and fp8, with and without rotation, 1-4 new tokens
+across page boundaries, fresh pages, kept and raised fp8 scales), the rotated q,
+repeated appends, e4m3fn special values, and a decode step over the appended cache
+against the fp64 decode oracle."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import append as OA
+from tests.gpu_util import device_inputs, log, run_decode
+from tests.test_gpu_parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_gqa_amd  # noqa: F401  (fails loudly without the built library)
+
+
+def cfg(**kw):
+    base = dict(name="append", batch=0, seq_lens=(1,), q_len=1, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, page_size=16, kv_format="bf16")
+    base.update(kw)
+    return base
+
+
+def gpu_append(inp, dev, k_new, v_new, q, rope):
+    """Run pkv_kv_append on the device copies in ``dev`` (updated in place); returns the
+    rotated q bits (or None)."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    kn, vn = t(k_new), t(v_new)
+    qd = t(q) if rope is not None else None
+    q_out = torch.empty_like(qd) if qd is not None else None
+    cos = sin = None
+    if rope is not None:
+        cos, sin = (torch.from_numpy(x).cuda() for x in rope)
+    pkv.pkv_kv_append(k_new=kn, v_new=vn, k_cache=dev["k"], v_cache=dev["v"], block_table=dev["bt"],
+                      seq_lens=dev["sl"], num_pages=dev["k"].shape[0], batch=inp.batch,
+                      q_len=inp.q_len, num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
+                      head_dim=inp.head_dim, page_size=inp.page_size, bt_stride=inp.block_table.shape[1],
+                      kv_format=inp.kv_format, q=qd, q_out=q_out, rope_cos=cos, rope_sin=sin,
+                      max_pos=0 if rope is None else rope[0].shape[0], k_scale=dev["ks"], v_scale=dev["vs"])
+    torch.cuda.synchronize()
+    return None if q_out is None else q_out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cache_bits(dev, inp):
+    import torch
+    if inp.kv_format == "bf16":
+        f = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)
+        return f(dev["k"]), f(dev["v"]), None, None
+    return dev["k"].cpu().numpy(), dev["v"].cpu().numpy(), dev["ks"].cpu().numpy(), dev["vs"].cpu().numpy()
+
+
+def oracle_append(inp, k_new, v_new, q, rope):
+    cos, sin = rope if rope is not None else (None, None)
+    q_out = OA.kv_append(inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale, inp.block_table,
+                         inp.seq_lens, k_new, v_new, q=q, cos=cos, sin=sin, kv_format=inp.kv_format)
+    return q_out
+
+
+def assert_same(inp, dev, q_gpu, q_ref, tag):
+    k, v, ks, vs = cache_bits(dev, inp)
+    assert np.array_equal(k, inp.k_cache), tag + " k cache"
+    assert np.array_equal(v, inp.v_cache), tag + " v cache"
+    if ks is not None:
+        for name, got, want in (("k_scale", ks, inp.k_scale), ("v_scale", vs, inp.v_scale)):
+            bad = np.argwhere(got != want)
+            for phys, g in bad[:8]:
+                log("  %s %s[%d, %d]: gpu %r (%08x) oracle %r (%08x)" % (
+                    tag, name, phys, g, float(got[phys, g]), got[phys, g:g + 1].view(np.uint32)[0],
+                    float(want[phys, g]), want[phys, g:g + 1].view(np.uint32)[0]))
+            assert len(bad) == 0, tag + " " + name
+    if q_ref is not None:
+        assert np.array_equal(q_gpu, q_ref), tag + " q"
+
+
+CASES = [
+    dict(id="bf16_p16_t1", c=cfg(), rope=False),
+    dict(id="bf16_p16_t4_rope", c=cfg(q_len=4), rope=True),
+    dict(id="bf16_p32_d64_t3_rope", c=cfg(q_len=3, page_size=32, head_dim=64, num_q_heads=8, num_kv_heads=8), rope=True),
+    dict(id="fp8_t1", c=cfg(kv_format="fp8", page_size=64), rope=False),
+    dict(id="fp8_t2_rope", c=cfg(kv_format="fp8", page_size=64, q_len=2), rope=True),
+    dict(id="fp8_t4_rope_g4", c=cfg(kv_format="fp8", page_size=64, q_len=4, num_q_heads=16, num_kv_heads=4), rope=True),
+    dict(id="fp8_t3_d64", c=cfg(kv_format="fp8", page_size=64, q_len=3, head_dim=64), rope=False),
+]
+# lengths hitting fresh pages (L - Tq on a page boundary), page-spanning new tokens,
+# and pages with earlier tokens
+LENS = [1, 4, 17, 63, 64, 65, 66, 67, 128, 130, 200, 1000]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["id"] for c in CASES])
+def test_append_matches_oracle(case):
+    c = case["c"]
+    inp = synth.make_inputs(c, seed=31, slack_pages=3, seq_lens=[max(x, c["q_len"]) for x in LENS])
+    # half the (request, kv head) groups far beyond their pages' range: fp8 scales rise
+    scale = np.where(np.random.default_rng(32).random((inp.batch, inp.num_kv_heads)) < 0.5, 1.0, 3e3)
+    k_new, v_new, q = synth.new_token_rows(inp, seed=33, scale=scale)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim) if case["rope"] else None
+    dev = device_inputs(inp)
+    log("append case %s" % case["id"])
+    q_gpu = gpu_append(inp, dev, k_new, v_new, q, rope)
+    q_ref = oracle_append(inp, k_new, v_new, q, rope)
+    assert_same(inp, dev, q_gpu, q_ref, case["id"])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_repeated_appends_match_oracle(fmt):
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2)
+    lens = np.array([2, 61, 62, 63, 126, 300], np.int32)
+    inp = synth.make_inputs(c, seed=34, slack_pages=4, seq_lens=lens + 2 * 8)   # room for 8 steps
+    inp.seq_lens[:] = lens
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    dev = device_inputs(inp)
+    import torch
+    for step in range(8):
+        dev["sl"].copy_(torch.from_numpy(inp.seq_lens))
+        k_new, v_new, q = synth.new_token_rows(inp, seed=40 + step, scale=1.0 + 3 * step)
+        q_gpu = gpu_append(inp, dev, k_new, v_new, q, rope)
+        q_ref = oracle_append(inp, k_new, v_new, q, rope)
+        assert_same(inp, dev, q_gpu, q_ref, "step %d" % step)
+        inp.seq_lens += 2
+
+
+def test_fp8_special_values_encode_exactly():
+    """Rows whose largest value is 448 get scale 1 on a fresh page, so every other
+    value is encoded as itself: grid midpoints (ties), subnormals, negative tiny values
+    (-> 0x80), values between the last two grid points."""
+    from oracle.formats import E4M3FN_TABLE
+    c = cfg(kv_format="fp8", page_size=64, head_dim=128, num_kv_heads=1, num_q_heads=4)
+    inp = synth.make_inputs(c, seed=35, slack_pages=2, seq_lens=[65, 129, 193])   # fresh pages
+    grid = E4M3FN_TABLE[:0x7F]
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([mids, -mids, [-2.0 ** -100, -0.0, 0.0, 2.0 ** -10, 3 * 2.0 ** -10, 440, 444]])
+    rows = []
+    for b in range(3):
+        r = np.resize(vals[b * 127:], 128).astype(np.float32)
+        r[0] = 448.0
+        rows.append(r)
+    x = np.stack(rows)[:, None, None, :]                       # [B, Tq=1, Hkv=1, D]
+    kb = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(OA.bf16_bits_to_f64(kb).astype(np.float32), x.astype(np.float32))
+    dev = device_inputs(inp)
+    gpu_append(inp, dev, kb, kb, None, None)
+    oracle_append(inp, kb, kb, None, None)
+    assert_same(inp, dev, None, None, "special values")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_after_append_matches_oracle(fmt):
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=4, num_q_heads=16,
+            num_kv_heads=4)
+    inp = synth.make_inputs(c, seed=36, slack_pages=2, seq_lens=[4, 70, 500, 2000, 3000])
+    k_new, v_new, q = synth.new_token_rows(inp, seed=37)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    dev = device_inputs(inp)
+    gpu_append(inp, dev, k_new, v_new, q, rope)
+    q_rot = oracle_append(inp, k_new, v_new, q, rope)          # inp now holds the appended cache
+    inp.q = q_rot
+    import torch
+    dev["q"] = torch.from_numpy(q_rot.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse, _ = run_decode(inp, dev=dev)
+    check(inp, out, lse, tag="append + decode " + fmt)
