@@ -50,6 +50,36 @@ FP8_SPEC = dict(
 
 ALL = {c["name"]: c for c in (TINY, LLAMA8B, MIXED, LONG, FP8_SPEC)}
 
+# Variable-length prefill over the same paged cache. ``q_lens`` is a recipe like
+# ``seq_lens`` above; ``prefix`` (the tokens already in the cache before the chunk,
+# 0 for a whole prompt) is a fixed tuple or a recipe; kv length = prefix + q length.
+PREFILL_VARLEN = dict(
+    name="prefill_varlen",
+    desc="variable-length prefill: B=8 prompts, lengths log-uniform in [128, 16384] "
+         "(seed 0), 32 q / 8 kv heads, D=128, page 16, bf16 KV, causal",
+    batch=8, q_lens=("loguniform", 128, 16384), prefix=("const", 0),
+    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, kv_format="bf16",
+)
+
+PREFILL_LONG = dict(
+    name="prefill_long",
+    desc="long prefill: one 65536-token prompt, 32 q / 8 kv heads, D=128, page 64, "
+         "bf16 KV, causal",
+    batch=1, q_lens=("const", 65536), prefix=("const", 0),
+    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, kv_format="bf16",
+)
+
+PREFILL_CHUNK_FP8 = dict(
+    name="prefill_chunk_fp8",
+    desc="chunked prefill over an FP8 cache: B=4 chunks of 2048 tokens after prefixes "
+         "uniform in [0, 16384] (seed 0), 32 q / 8 kv heads, D=128, page 64, e4m3fn KV "
+         "with per-page scales, causal",
+    batch=4, q_lens=("const", 2048), prefix=("uniform_int", 0, 16384),
+    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, kv_format="fp8",
+)
+
+ALL_PREFILL = {c["name"]: c for c in (PREFILL_VARLEN, PREFILL_LONG, PREFILL_CHUNK_FP8)}
+
 
 def softmax_scale(head_dim):
     """1/sqrt(head_dim), the scale every workload uses (passed to both sides as fp32)."""

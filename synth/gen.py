@@ -179,6 +179,57 @@ def make_inputs(cfg, seed=0, poison=False, slack_pages=0, seq_lens=None):
     return inp
 
 
+@dataclass
+class PrefillInputs:
+    cache: DecodeInputs       # seq_lens = kv lengths (prefix + query tokens), block table, pools
+    q: np.ndarray             # uint16 bf16 bits [total_q, Hq, D], requests packed in order
+    q_lens: np.ndarray        # int32 [B]
+    cu_q: np.ndarray          # int32 [B + 1], prefix sums of q_lens
+
+    @property
+    def batch(self):
+        return int(self.q_lens.shape[0])
+
+
+def make_prefill_inputs(cfg, seed=0, q_lens=None, prefix=None, poison=False, slack_pages=0):
+    """Draw a prefill batch: q lengths then prefixes from ``default_rng(seed)`` (recipes
+    as for seq_lens), the cache of kv lengths prefix + q length from ``make_inputs``
+    with seed + 1, then the packed q (standard normal, bf16) from ``default_rng(seed +
+    2)``. ``q_lens`` / ``prefix`` override the recipes."""
+    rng = np.random.default_rng(seed)
+    B = cfg["batch"]
+    if q_lens is None:
+        q_lens = draw_seq_lens(dict(batch=B, seq_lens=cfg["q_lens"]), rng)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    B = int(q_lens.shape[0])
+    if prefix is None:
+        prefix = draw_seq_lens(dict(batch=B, seq_lens=cfg["prefix"]), rng)
+    prefix = np.asarray(prefix, dtype=np.int32)
+    kv = (q_lens + prefix).astype(np.int32)
+    cache_cfg = dict(cfg, q_len=1, seq_lens=tuple(int(x) for x in kv), batch=B)
+    cache = make_inputs(cache_cfg, seed=seed + 1, poison=poison, slack_pages=slack_pages)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    total = int(cu[-1])
+    rq = np.random.default_rng(seed + 2)
+    H, D = cfg["num_q_heads"], cfg["head_dim"]
+    q = f32_to_bf16_bits(rq.standard_normal(total * H * D, dtype=np.float32)).reshape(total, H, D)
+    return PrefillInputs(cache=cache, q=q, q_lens=q_lens, cu_q=cu)
+
+
+def prefill_flops(inp):
+    """Algorithmic flops of causal prefill attention: 4 * D * Hq per (query, visible
+    key) pair (Q.K and P.V, multiply-add = 2), query t of request b seeing
+    prefix_b + t + 1 keys."""
+    c = inp.cache
+    pairs = 0
+    for b in range(inp.batch):
+        n = int(inp.q_lens[b])
+        pre = int(c.seq_lens[b]) - n
+        pairs += n * pre + n * (n + 1) // 2
+    return 4 * c.head_dim * c.num_q_heads * pairs
+
+
 def apply_poison(inp):
     """Overwrite every element that no valid token reads with NaN bits."""
     nan = BF16_NAN if inp.kv_format == "bf16" else FP8_NAN
