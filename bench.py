@@ -75,6 +75,140 @@ def cpu_baseline(inp, algo_bytes):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+PREFILL_METRIC = "causal prefill attention TFLOP/s over the paged KV cache"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD's published figure
+
+
+def prefill_cpu_baseline(p, stride=16):
+    """Time the fp64 CPU oracle on a sample of the prefill workload: kv head 0 of
+    every request, every ``stride``-th query token (flops counted for those rows)."""
+    import numpy as np
+    from oracle.prefill import prefill_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    c = p.cache
+    G = c.num_q_heads // c.num_kv_heads
+    rows, flops = {}, 0
+    for b in range(p.batch):
+        n, L = int(p.q_lens[b]), int(c.seq_lens[b])
+        rows[b] = list(range(0, n, stride))
+        flops += sum(4 * c.head_dim * G * (L - n + t + 1) for t in rows[b])
+    log("cpu baseline: timing the oracle on kv head 0, every %d-th token" % stride)
+    t0 = time.perf_counter()
+    prefill_attention(p, pairs=[(b, 0) for b in range(p.batch)], rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "kv head 0 of every request, every %d-th query token (%.3g flops), "
+                      "fp64 numpy, host cores" % (stride, flops),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def prefill_main(args):
+    """One step = host tile plan (copied to the device) + the prefill kernel over one
+    batch of the named prefill workload."""
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_gqa_amd as pkv
+
+    cfg = synth.ALL_PREFILL[args.prefill]
+    log("generating %s inputs (seed %d)" % (args.prefill, args.seed))
+    p = synth.make_prefill_inputs(cfg, seed=args.seed)
+    c = p.cache
+    flops = synth.prefill_flops(p)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    qd = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if c.kv_format == "bf16":
+        k = torch.from_numpy(c.k_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(c.v_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        k, v = torch.from_numpy(c.k_cache).to(dev), torch.from_numpy(c.v_cache).to(dev)
+        ks, vs = torch.from_numpy(c.k_scale).to(dev), torch.from_numpy(c.v_scale).to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    cu = torch.from_numpy(p.cu_q).to(dev)
+    kl = torch.from_numpy(c.seq_lens).to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((int(p.cu_q[-1]), c.num_q_heads), dtype=torch.float32, device=dev)
+    runner = pkv.PagedPrefill(num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
+                              head_dim=c.head_dim, page_size=c.page_size, kv_format=c.kv_format)
+    q_lens_h, kv_lens_h = p.q_lens.copy(), c.seq_lens.copy()
+
+    def step(evs=None):
+        items = runner.plan(q_lens_h, kv_lens_h)
+        if evs is not None:
+            evs[0].record()
+        runner(qd, cu, kl, bt, q_lens_h, kv_lens_h, c.scale, k_cache=k, v_cache=v, k_scale=ks,
+               v_scale=vs, out=out, lse=lse, items=items)
+        if evs is not None:
+            evs[1].record()
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log("timing %d steps" % K)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    value = flops / (wall / K) / 1e12
+    achieved = flops / kern_s / 1e12
+    n_items = int(runner.last_items.shape[0])
+    log("%.1f us/step, %.1f TFLOP/s; prefill kernel %.1f us avg (%.1f TFLOP/s, %.1f%% of bf16 peak)"
+        % (wall / K * 1e6, value, kern_s * 1e6, achieved, 100 * achieved / MFMA_BF16_PEAK_TFLOPS))
+    rec = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.kv_format == "bf16" else "fp8 KV, bf16 MFMA",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg["desc"],
+            "batch": p.batch,
+            "q_lens": p.q_lens.tolist(),
+            "kv_lens": c.seq_lens.tolist(),
+            "heads": "%d q / %d kv" % (c.num_q_heads, c.num_kv_heads),
+            "head_dim": c.head_dim,
+            "page_size": c.page_size,
+            "work_items": n_items,
+            "flops_per_step": flops,
+            "step": "host tile plan (copied to the device) + prefill kernel",
+        },
+        "roofline": {
+            "kernel": "prefill",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(kern_s * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefill_cpu_baseline(p)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,11 +232,17 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--prefill", default=None, metavar="WORKLOAD",
+                    help="time variable-length causal prefill on a prefill workload "
+                         "(prefill_varlen, prefill_long, prefill_chunk_fp8) instead of decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.prefill is not None:
+        prefill_main(args)
+        return
 
     import numpy as np
     import torch

@@ -331,6 +331,59 @@ typedef struct pkv_kv_append_args {
  */
 int pkv_kv_append(const pkv_kv_append_args* args, void* stream);
 
+/*
+ * Variable-length causal prefill over the paged cache (the HALOps README's
+ * variable-length GQA prefill; the HPC-Ops launch article measures prefill for 128 to
+ * 64K input tokens). A batch packs the query rows of B requests: q [total, Hq, D],
+ * request b's rows at cu_q[b] .. cu_q[b+1]-1. Request b's n_b = cu_q[b+1] - cu_q[b]
+ * query tokens are the last n_b of its kv_lens[b] cached tokens (a whole prompt, or a
+ * chunk after a prefix), so its query t attends to keys j <= kv_lens[b] - n_b + t.
+ * The cache, block table, GQA head mapping and FP8 scales are those of decode.
+ *
+ * Work items (host): one per (request, kv head, head group, 64-token query tile); a
+ * head group is min(G, 4) query heads of the kv head (G must be 1, 2 or a multiple of
+ * 4). pkv_prefill_plan lists them heaviest first (most keys, ties by (b, g, group,
+ * tile)) as int32 [N][4] = (b, g, group, first token); pkv_prefill_plan_size gives N.
+ * Errors: INVALID_ARG (null pointer, sizes, n_b > kv_len_b or n_b < 0), UNSUPPORTED
+ * (G not 1, 2 or a multiple of 4).
+ */
+int pkv_prefill_plan_size(int batch, const int32_t* q_lens_h, int num_q_heads, int num_kv_heads,
+                          int64_t* num_items_out);
+int pkv_prefill_plan(int batch, const int32_t* q_lens_h, const int32_t* kv_lens_h, int num_q_heads,
+                     int num_kv_heads, int32_t* items_h);
+
+/* Arguments of pkv_prefill (pointers device-accessible, caller-owned). */
+typedef struct pkv_prefill_args {
+  size_t struct_size;             /* sizeof(pkv_prefill_args) */
+  const void* q;                  /* bf16 [total, Hq, D] */
+  const int32_t* cu_q;            /* int32 [B + 1] */
+  const int32_t* kv_lens;         /* int32 [B] (each >= n_b) */
+  const int32_t* block_table;     /* int32 [B, bt_stride] */
+  const int32_t* items;           /* int32 [num_items][4] from pkv_prefill_plan, 16-byte aligned */
+  const void* k_cache;            /* [num_pages, Hkv, P, D], bf16 or e4m3fn */
+  const void* v_cache;
+  const float* k_scale;           /* fp32 [num_pages, Hkv]; NULL iff bf16 */
+  const float* v_scale;
+  void* out;                      /* bf16 [total, Hq, D] */
+  float* lse;                     /* fp32 [total, Hq] (natural log) or NULL */
+  int64_t num_items;
+  int64_t num_pages;
+  int batch, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride;
+  int kv_format;                  /* enum pkv_kv_format */
+  float scale;                    /* softmax scale */
+} pkv_prefill_args;
+
+/*
+ * Enqueue the prefill kernel: one workgroup per work item; for its 64 query tokens and
+ * head group it walks the causal key range in 32-key blocks with an online softmax
+ * and writes each row's normalised output (bf16) and log-sum-exp. Every row of every
+ * request must be covered by the items (pkv_prefill_plan's list). Enqueue only.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not 64/128, P not a multiple of 16, fp8 with
+ * P != 64, G not 1, 2 or a multiple of 4), ALIGNMENT (q, out, caches, items 16 bytes),
+ * HIP.
+ */
+int pkv_prefill(const pkv_prefill_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,6 +83,22 @@ class KvAppendArgs(ctypes.Structure):
     ]
 
 
+class PrefillArgs(ctypes.Structure):
+    """Mirror of ``pkv_prefill_args`` (include/pkv.h)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("cu_q", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("items", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("num_items", ctypes.c_int64), ("num_pages", ctypes.c_int64),
+        ("batch", ctypes.c_int), ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int), ("bt_stride", ctypes.c_int),
+        ("kv_format", ctypes.c_int), ("scale", ctypes.c_float),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libpkv.so is not built (expected at %s); run "
@@ -122,6 +138,9 @@ def _load():
         "pkv_block_sparse_lengths": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_void_p, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]),
         "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(KvAppendArgs), ctypes.c_void_p]),
+        "pkv_prefill_plan_size": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, _i64p]),
+        "pkv_prefill_plan": (ctypes.c_int, [ctypes.c_int, _i32p, _i32p, ctypes.c_int, ctypes.c_int, _i32p]),
+        "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]),
         "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -348,6 +367,82 @@ def pkv_kv_append(*, k_new, v_new, k_cache, v_cache, block_table, seq_lens, num_
     a.kv_format = KV_FORMATS.get(kv_format, kv_format)
     a.max_pos = max_pos
     _check(_lib.pkv_kv_append(ctypes.byref(a), _stream_handle(stream)), "pkv_kv_append")
+
+
+def pkv_prefill_plan_size(q_lens_h, num_q_heads, num_kv_heads):
+    ql, qlp = _i32(q_lens_h)
+    n = ctypes.c_int64()
+    _check(_lib.pkv_prefill_plan_size(len(ql), qlp, num_q_heads, num_kv_heads, ctypes.byref(n)),
+           "pkv_prefill_plan_size")
+    return n.value
+
+
+def pkv_prefill_plan(q_lens_h, kv_lens_h, num_q_heads, num_kv_heads):
+    """Prefill work items, int32 [N, 4] rows (b, g, head group, first token), heaviest
+    first."""
+    ql, qlp = _i32(q_lens_h)
+    kl, klp = _i32(kv_lens_h)
+    n = pkv_prefill_plan_size(ql, num_q_heads, num_kv_heads)
+    items = np.empty((n, 4), np.int32)
+    _check(_lib.pkv_prefill_plan(len(ql), qlp, klp, num_q_heads, num_kv_heads,
+                                 items.ctypes.data_as(_i32p)), "pkv_prefill_plan")
+    return items
+
+
+def pkv_prefill(*, q, cu_q, kv_lens, block_table, items, num_items, k_cache, v_cache, out,
+                num_pages, batch, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
+                kv_format, scale, k_scale=None, v_scale=None, lse=None, stream=None):
+    """Enqueue variable-length causal prefill over the paged cache."""
+    a = PrefillArgs()
+    a.struct_size = ctypes.sizeof(PrefillArgs)
+    a.q, a.cu_q, a.kv_lens = _ptr(q, "q"), _ptr(cu_q, "cu_q"), _ptr(kv_lens, "kv_lens")
+    a.block_table, a.items = _ptr(block_table, "block_table"), _ptr(items, "items")
+    a.k_cache, a.v_cache = _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
+    a.k_scale, a.v_scale = _ptr(k_scale, "k_scale"), _ptr(v_scale, "v_scale")
+    a.out, a.lse = _ptr(out, "out"), _ptr(lse, "lse")
+    a.num_items, a.num_pages, a.batch = num_items, num_pages, batch
+    a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
+    a.page_size, a.bt_stride = page_size, bt_stride
+    a.kv_format = KV_FORMATS.get(kv_format, kv_format)
+    a.scale = scale
+    _check(_lib.pkv_prefill(ctypes.byref(a), _stream_handle(stream)), "pkv_prefill")
+
+
+class PagedPrefill:
+    """Variable-length causal prefill over the paged cache: host tile plan (copied to the
+    device on the current stream) + the prefill kernel."""
+
+    def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, kv_format="bf16",
+                 device=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.head_dim, self.page_size, self.kv_format = head_dim, page_size, kv_format
+        self.last_items = None
+
+    def plan(self, q_lens_h, kv_lens_h):
+        items = pkv_prefill_plan(q_lens_h, kv_lens_h, self.num_q_heads, self.num_kv_heads)
+        self.last_items = items
+        return self.torch.from_numpy(items).to(self.device, non_blocking=False)
+
+    def __call__(self, q, cu_q, kv_lens, block_table, q_lens_h, kv_lens_h, scale, *, k_cache,
+                 v_cache, k_scale=None, v_scale=None, out=None, lse=None, items=None, stream=None):
+        """q bf16 [total, Hq, D]; cu_q / kv_lens device int32; q_lens_h / kv_lens_h host
+        copies (for the plan). ``items``: a device plan from ``plan`` to reuse."""
+        torch = self.torch
+        if items is None:
+            items = self.plan(q_lens_h, kv_lens_h)
+        if out is None:
+            out = torch.empty_like(q)
+        pkv_prefill(q=q, cu_q=cu_q, kv_lens=kv_lens, block_table=block_table, items=items,
+                    num_items=items.shape[0], k_cache=k_cache, v_cache=v_cache, out=out,
+                    num_pages=k_cache.shape[0], batch=int(cu_q.shape[0]) - 1,
+                    num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads,
+                    head_dim=self.head_dim, page_size=self.page_size,
+                    bt_stride=block_table.shape[1], kv_format=self.kv_format, scale=scale,
+                    k_scale=k_scale, v_scale=v_scale, lse=lse, stream=stream)
+        return out
 
 
 # ---------------------------------------------------------------------------------

@@ -14,7 +14,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
 SOURCES = ["planner.cpp", "api.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip",
-           "block_sparse.hip", "kv_append.hip"]
+           "block_sparse.hip", "kv_append.hip", "prefill.hip"]
 HEADERS = ["planner.hpp", "kernels.hpp"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

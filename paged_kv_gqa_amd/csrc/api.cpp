@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -11,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 #include "planner.hpp"
@@ -480,6 +482,131 @@ int pkv_kv_append(const pkv_kv_append_args* a, void* stream) {
   p.fp8 = fp8;
   const hipError_t e = pkv::launch_kv_append(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+namespace {
+
+int prefill_heads_per_item(int num_q_heads, int num_kv_heads) {
+  const int G = num_q_heads / num_kv_heads;
+  return G < pkv::kPrefillMaxHeadsPerItem ? G : pkv::kPrefillMaxHeadsPerItem;
+}
+
+int check_prefill_heads(int num_q_heads, int num_kv_heads) {
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G % 4 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, multiples of 4)", G);
+  return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_prefill_plan_size(int batch, const int32_t* q_lens_h, int num_q_heads, int num_kv_heads,
+                          int64_t* num_items_out) {
+  if (batch < 0 || num_items_out == nullptr || (batch > 0 && q_lens_h == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "bad arguments");
+  const int st = check_prefill_heads(num_q_heads, num_kv_heads);
+  if (st != PKV_OK) return st;
+  const int groups = (num_q_heads / num_kv_heads) / prefill_heads_per_item(num_q_heads, num_kv_heads);
+  int64_t n = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (q_lens_h[b] < 0) return fail(PKV_ERR_INVALID_ARG, "q_lens[%d] = %d < 0", b, q_lens_h[b]);
+    n += pkv::ceil_div(q_lens_h[b], pkv::kPrefillTileTokens);
+  }
+  *num_items_out = n * num_kv_heads * groups;
+  return PKV_OK;
+}
+
+int pkv_prefill_plan(int batch, const int32_t* q_lens_h, const int32_t* kv_lens_h, int num_q_heads,
+                     int num_kv_heads, int32_t* items_h) {
+  int64_t total = 0;
+  int st = pkv_prefill_plan_size(batch, q_lens_h, num_q_heads, num_kv_heads, &total);
+  if (st != PKV_OK) return st;
+  if (total > 0 && (kv_lens_h == nullptr || items_h == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (total > INT32_MAX / 4) return fail(PKV_ERR_UNSUPPORTED, "too many prefill items");
+  const int groups = (num_q_heads / num_kv_heads) / prefill_heads_per_item(num_q_heads, num_kv_heads);
+  struct Item {
+    int64_t keys;
+    int32_t b, g, hg, t0;
+  };
+  std::vector<Item> v;
+  v.reserve(static_cast<size_t>(total));
+  for (int b = 0; b < batch; ++b) {
+    const int n = q_lens_h[b], L = kv_lens_h[b];
+    if (L < n) return fail(PKV_ERR_INVALID_ARG, "kv_lens[%d] = %d < q_len %d", b, L, n);
+    for (int t0 = 0; t0 < n; t0 += pkv::kPrefillTileTokens) {
+      const int64_t keys = static_cast<int64_t>(L - n) + std::min(t0 + pkv::kPrefillTileTokens, n);
+      for (int g = 0; g < num_kv_heads; ++g)
+        for (int hg = 0; hg < groups; ++hg) v.push_back({keys, b, g, hg, t0});
+    }
+  }
+  // Heaviest first; the stable sort keeps (b, g, group, tile) order among equals.
+  std::stable_sort(v.begin(), v.end(), [](const Item& x, const Item& y) { return x.keys > y.keys; });
+  for (size_t i = 0; i < v.size(); ++i) {
+    items_h[4 * i + 0] = v[i].b;
+    items_h[4 * i + 1] = v[i].g;
+    items_h[4 * i + 2] = v[i].hg;
+    items_h[4 * i + 3] = v[i].t0;
+  }
+  return PKV_OK;
+}
+
+int pkv_prefill(const pkv_prefill_args* a, void* stream) {
+  if (a == nullptr) return fail(PKV_ERR_INVALID_ARG, "null args");
+  if (a->struct_size < sizeof(pkv_prefill_args))
+    return fail(PKV_ERR_INVALID_ARG, "struct_size %zu < %zu", a->struct_size, sizeof(pkv_prefill_args));
+  if (a->kv_format != PKV_KV_BF16 && a->kv_format != PKV_KV_FP8_E4M3FN)
+    return fail(PKV_ERR_INVALID_ARG, "kv_format %d is not a pkv_kv_format", a->kv_format);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", a->head_dim);
+  if (a->page_size < 16 || a->page_size % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", a->page_size);
+  const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
+  if (fp8 && a->page_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "fp8 KV needs page_size 64, got %d", a->page_size);
+  int st = check_prefill_heads(a->num_q_heads, a->num_kv_heads);
+  if (st != PKV_OK) return st;
+  if (a->batch < 0 || a->num_items < 0 || a->num_pages < 0 || a->bt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes out of range");
+  if (a->num_items == 0) return PKV_OK;
+  if (a->num_items > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many prefill items");
+  if (!a->q || !a->cu_q || !a->kv_lens || !a->block_table || !a->items || !a->k_cache ||
+      !a->v_cache || !a->out)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (fp8 != (a->k_scale != nullptr) || fp8 != (a->v_scale != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale must be given exactly for fp8 KV");
+  if (!std::isfinite(a->scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k_cache, 16) ||
+      !aligned(a->v_cache, 16) || !aligned(a->items, 16) || !aligned(a->cu_q, 4) ||
+      !aligned(a->kv_lens, 4) || !aligned(a->block_table, 4) || (a->lse && !aligned(a->lse, 4)))
+    return fail(PKV_ERR_ALIGNMENT, "q, out, caches and items need 16 bytes");
+  pkv::PrefillParams p;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.cu_q = a->cu_q;
+  p.kv_lens = a->kv_lens;
+  p.block_table = a->block_table;
+  p.items = a->items;
+  p.k_cache = static_cast<const uint8_t*>(a->k_cache);
+  p.v_cache = static_cast<const uint8_t*>(a->v_cache);
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.lse = a->lse;
+  p.num_items = a->num_items;
+  p.batch = a->batch;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.page_size = a->page_size;
+  p.bt_stride = a->bt_stride;
+  p.scale = a->scale;
+  const hipError_t e = pkv::launch_prefill(p, a->head_dim, fp8,
+                                           prefill_heads_per_item(a->num_q_heads, a->num_kv_heads),
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }
 

@@ -75,6 +75,30 @@ struct KvAppendParams {
 
 hipError_t launch_kv_append(const KvAppendParams& p, hipStream_t stream);
 
+// Query tokens per prefill work item, and query heads one item covers at most.
+constexpr int kPrefillTileTokens = 64;
+constexpr int kPrefillMaxHeadsPerItem = 4;
+
+struct PrefillParams {
+  const uint16_t* q;             // bf16 [total, Hq, D]
+  const int32_t* cu_q;           // [B + 1]
+  const int32_t* kv_lens;        // [B]
+  const int32_t* block_table;    // [B, bt_stride]
+  const int32_t* items;          // [num_items][4] (b, g, head group, first token)
+  const uint8_t* k_cache;        // [num_pages, Hkv, P, D] bf16 or e4m3fn
+  const uint8_t* v_cache;
+  const float* k_scale;          // [num_pages, Hkv] (fp8)
+  const float* v_scale;
+  uint16_t* out;                 // bf16 [total, Hq, D]
+  float* lse;                    // [total, Hq] or null
+  int64_t num_items;
+  int batch, num_q_heads, num_kv_heads, page_size, bt_stride;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, int heads_per_item,
+                          hipStream_t stream);
+
 // Device planner limits: one thread per worker, the requests sorted in LDS.
 constexpr int kMaxDevicePlanWorkers = 1024;
 constexpr int kMaxDevicePlanBatch = 4096;

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -321,6 +321,61 @@ def test_request_split_must_divide_the_batch():
                               req_tile_base=8 * A, batch=6, q_len=1, num_q_heads=4, num_kv_heads=1,
                               head_dim=128, request_split=4, out=A, stream=0)
     assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_prefill_plan_lists_tiles_heaviest_first():
+    q_lens, kv_lens = [70, 1, 130], [70, 40, 200]
+    items = pkv.pkv_prefill_plan(q_lens, kv_lens, 16, 2)       # G = 8: 2 head groups of 4
+    want = []
+    for b, (n, L) in enumerate(zip(q_lens, kv_lens)):
+        for t0 in range(0, n, 64):
+            keys = L - n + min(t0 + 64, n)
+            for g in range(2):
+                for hg in range(2):
+                    want.append((-keys, b, g, hg, t0))
+    want.sort()
+    assert items.tolist() == [[b, g, hg, t0] for _, b, g, hg, t0 in want]
+    assert pkv.pkv_prefill_plan_size(q_lens, 16, 2) == len(want)
+    assert pkv.pkv_prefill_plan([3], [3], 4, 4).tolist() == [[0, 0, 0, 0], [0, 1, 0, 0], [0, 2, 0, 0],
+                                                             [0, 3, 0, 0]]
+
+
+def test_prefill_plan_errors():
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefill_plan([5], [4], 8, 2)                    # kv shorter than the queries
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefill_plan([5], [5], 6, 2)                    # G = 3
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+
+
+def prefill_kwargs(**kw):
+    base = dict(q=A, cu_q=2 * A, kv_lens=3 * A, block_table=4 * A, items=5 * A, num_items=4,
+                k_cache=6 * A, v_cache=7 * A, out=8 * A, num_pages=16, batch=2, num_q_heads=8,
+                num_kv_heads=2, head_dim=128, page_size=16, bt_stride=4, kv_format="bf16",
+                scale=0.1, stream=0)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(page_size=8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),                  # fp8 needs page 64
+    (dict(kv_format="fp8", page_size=64), pkv.PKV_ERR_INVALID_ARG),    # no scales
+    (dict(num_q_heads=6), pkv.PKV_ERR_UNSUPPORTED),                    # G = 3
+    (dict(items=5 * A + 4), pkv.PKV_ERR_ALIGNMENT),
+    (dict(scale=float("inf")), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_prefill_argument_errors(kw, status):
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefill(**prefill_kwargs(**kw))
+    assert e.value.status == status
+
+
+def test_prefill_without_items_is_a_no_op():
+    pkv.pkv_prefill(**prefill_kwargs(num_items=0))
 
 
 def append_kwargs(**kw):
