@@ -17,19 +17,25 @@
 // - Online softmax in log2 units, c = scale * log2(e) (times the page's K scale for
 //   FP8): p = 2^(s c - m) with one fused multiply-add before the exponential. The
 //   running maximum m is raised only when a block exceeds it by more than 8, so the
-//   accumulator is rescaled rarely; the row's probability sum l is kept in fp32 and
-//   is the output's normaliser and the log-sum-exp's argument.
+//   accumulator is rescaled rarely; the row's probability sum l is kept in fp32 (each
+//   lane sums its keys; the row's four lanes are added at the end) and is the output's
+//   normaliser and the log-sum-exp's argument.
 // - P enters the matrix cores as bf16. Where a block's largest probability may be a
 //   large share of the row's sum (a row's first block, rows that see few keys, sharp
 //   rows), the low bf16 part p - bf16(p) is multiplied into V as well, so the weights
 //   that dominate an output are carried to about 16 bits.
 // - O^T += V^T . P^T: the two S^T halves of a lane pack into the 8 k-values of P^T's
-//   B operand directly (keys 4gq + 0..3 and 16 + 4gq + 0..3); V is staged into LDS
-//   transposed, in that same key order, so V^T's A operand is one 16-byte LDS read.
+//   B operand directly (keys 4gq + 0..3 and 16 + 4gq + 0..3). V is staged row-major;
+//   gfx950's transposing LDS read (ds_read_b64_tr_b16: in each 16-lane group, lanes
+//   4k..4k+3 address row k of a 4 x 16 tile of 16-bit values and lane i receives
+//   column i) gives lane (n, gq) the four keys 4gq + 0..3 (then 16 + 4gq + 0..3) of
+//   head dim 16bl + n, i.e. V^T's A operand, in two reads.
 // - The next block's K and V are loaded into registers while the current one is
-//   computed (double-buffered stage, one barrier per block).
-// FP8 (e4m3fn) K/V bytes are widened to bf16 exactly; with 64-token pages a 32-key
-// block lies in one page, so its K scale multiplies the scores and its V scale P.
+//   computed (double-buffered stage, one barrier per block); the block-table entries
+//   are fetched one block earlier still.
+// FP8 (e4m3fn) K/V bytes are widened to bf16 exactly when staged, once per workgroup;
+// with 64-token pages a 32-key block lies in one page, so its K scale multiplies the
+// scores and its V scale P.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -91,13 +97,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Position of key k (0..31) of a block in the P^T / V^T operand order: lane group gq
-// holds keys 4gq + 0..3 of half 0 then of half 1.
-__device__ __forceinline__ int key_slot(int k) {
-  const int h = k >> 4, r = k & 15;
-  return 8 * (r >> 2) + 4 * h + (r & 3);
-}
-
 // Heads per work item GWI (1, 2, 4); each wave takes 16 tokens x HPW heads.
 template <int GWI>
 struct WaveCfg {
@@ -109,68 +108,86 @@ struct WaveCfg {
 template <int D, bool FP8>
 struct PCfg {
   static constexpr int kEb = FP8 ? 1 : 2;
-  static constexpr int kRowBytes = D * kEb;
-  static constexpr int kRowUnits = kRowBytes / 16;        // 16-byte units per K/V row
+  static constexpr int kRowBytes = D * kEb;               // one K or V row in the cache
+  static constexpr int kRowUnits = kRowBytes / 16;        // 16-byte units per cache row
   static constexpr int kBlockUnits = kBlockKeys * kRowUnits;
   static constexpr int kSteps = D / 32;                   // MFMA k-steps over D
   static constexpr int kDimBlocks = D / 16;               // 16-dim blocks of O^T
-  static constexpr int kDimsPerUnit = 16 / kEb;           // head dims in one 16-byte unit
 };
 
-// Head dimension of k-step s, lane group gq, element e (fp8: one 16-byte read of a
-// row serves two k-steps), as in the decode kernel.
-template <bool FP8>
-__device__ __forceinline__ int op_dim(int s, int gq, int e) {
-  if (FP8) return 64 * (s >> 1) + 16 * gq + 8 * (s & 1) + e;
-  return 32 * s + 8 * gq + e;
-}
+// Head dimension of k-step s, lane group gq, element e of the S^T operands.
+__device__ __forceinline__ int op_dim(int s, int gq, int e) { return 32 * s + 8 * gq + e; }
 
-// LDS (bytes): K rows [32] of kKStride = row bytes + 16, and V^T rows [D] of
-// kVStride = 80 (32 bf16 keys in operand order + 16). The padding puts the 16 rows
-// that 16 lanes read at once in disjoint bank groups, and leaves each lane one base
-// address with constant offsets.
-template <int D, bool FP8>
+// LDS (bytes), bf16 rows: K rows [32] of stride 2D + 16 (16 lanes reading one 16-byte
+// unit of rows n = 0..15 hit disjoint bank groups) and V rows [32] of stride 2D + 32
+// (the four rows of a transposing read hit disjoint bank groups). Each lane reads at
+// one base address plus constant offsets.
+template <int D>
 struct Stage {
-  static constexpr int kKStride = PCfg<D, FP8>::kRowBytes + 16;
-  static constexpr int kVStride = 2 * kBlockKeys + 16;
+  static constexpr int kKStride = 2 * D + 16;
+  static constexpr int kVStride = 2 * D + 32;
   alignas(16) uint8_t k[kBlockKeys * kKStride];
-  alignas(16) uint8_t vt[D * kVStride];
+  alignas(16) uint8_t v[kBlockKeys * kVStride];
 };
 
-struct TileCtx {
-  const int32_t* __restrict__ bt;
-  int64_t head_off, page_bytes;
-  int L, page_size, row_bytes;
-};
-
-// Global byte offset of 16-byte unit `unit` of key j (callers keep j < L).
-__device__ __forceinline__ int64_t unit_offset(const TileCtx& c, int j, int unit) {
-  const int page = j / c.page_size;
-  return static_cast<int64_t>(c.bt[page]) * c.page_bytes + c.head_off +
-         static_cast<int64_t>(j - page * c.page_size) * c.row_bytes + 16 * unit;
-}
-
-// 16-byte units of one block per thread (fp8 D=64 has fewer units than threads).
+// 16-byte cache units of one block per thread (fp8 with 512 threads: half the
+// threads stage nothing), with each unit's page walk: the physical page and in-page
+// row of the next block to load, and the logical page and in-page row of the block
+// after it (advanced by 32 keys per block, so no division by the page size).
 template <int D, bool FP8, int NT>
 struct BlockRegs {
   static constexpr int kUnits = (PCfg<D, FP8>::kBlockUnits + NT - 1) / NT;
   u32x4 k[kUnits];
   u32x4 v[kUnits];
+  int phys[kUnits], load_off[kUnits];
+  int walk_page[kUnits], walk_off[kUnits];
 };
+
+template <int D, bool FP8, int NT>
+__device__ __forceinline__ void walk_init(BlockRegs<D, FP8, NT>& r, int page_size, int tid) {
+  using C = PCfg<D, FP8>;
+#pragma unroll
+  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
+    const int row = (tid + NT * i) / C::kRowUnits;  // < 32 for staging units
+    r.walk_page[i] = row / page_size;
+    r.walk_off[i] = row % page_size;
+  }
+}
+
+// Look up the physical pages of the walked block (last_page clamps rows past the
+// sequence end, which are not loaded) and advance the walk by one block.
+template <int D, bool FP8, int NT>
+__device__ __forceinline__ void block_pages(BlockRegs<D, FP8, NT>& r, const int32_t* __restrict__ bt,
+                                            int last_page, int page_size, int tid) {
+  using C = PCfg<D, FP8>;
+#pragma unroll
+  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
+    const bool staged = tid + NT * i < C::kBlockUnits;
+    r.phys[i] = staged ? bt[min(r.walk_page[i], last_page)] : 0;
+    r.load_off[i] = r.walk_off[i];
+    int off = r.walk_off[i] + kBlockKeys, page = r.walk_page[i];
+    while (off >= page_size) {  // at most twice (page_size >= 16)
+      off -= page_size;
+      ++page;
+    }
+    r.walk_off[i] = off;
+    r.walk_page[i] = page;
+  }
+}
 
 // Load block kb's K and V units of this thread (zeros past the sequence end).
 template <int D, bool FP8, int NT>
-__device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const TileCtx& c,
-                                           const uint8_t* __restrict__ kc,
-                                           const uint8_t* __restrict__ vc, int kb, int tid) {
+__device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const uint8_t* __restrict__ kc,
+                                           const uint8_t* __restrict__ vc, int64_t page_bytes,
+                                           int64_t head_off, int kb, int L, int tid) {
   using C = PCfg<D, FP8>;
 #pragma unroll
   for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
     const int u = tid + NT * i;
     const int row = u / C::kRowUnits, unit = u % C::kRowUnits;
-    const int j = kb * kBlockKeys + row;
-    if (u < C::kBlockUnits && j < c.L) {
-      const int64_t off = unit_offset(c, j, unit);
+    if (u < C::kBlockUnits && kb * kBlockKeys + row < L) {
+      const int64_t off = static_cast<int64_t>(r.phys[i]) * page_bytes + head_off +
+                          r.load_off[i] * C::kRowBytes + 16 * unit;
       r.k[i] = *reinterpret_cast<const u32x4*>(kc + off);
       r.v[i] = *reinterpret_cast<const u32x4*>(vc + off);
     } else {
@@ -180,73 +197,74 @@ __device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const TileC
   }
 }
 
-// K rows as loaded; V transposed into operand key order (fp8 widened to bf16).
+// K and V rows into LDS as bf16 (fp8 widened exactly), row-major.
 template <int D, bool FP8, int NT>
-__device__ __forceinline__ void stage_block(Stage<D, FP8>& st, const BlockRegs<D, FP8, NT>& r, int tid) {
+__device__ __forceinline__ void stage_block(Stage<D>& st, const BlockRegs<D, FP8, NT>& r, int tid) {
   using C = PCfg<D, FP8>;
-  using S = Stage<D, FP8>;
+  using S = Stage<D>;
 #pragma unroll
   for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
     const int u = tid + NT * i;
     if (u >= C::kBlockUnits) break;
     const int row = u / C::kRowUnits, unit = u % C::kRowUnits;
-    *reinterpret_cast<u32x4*>(st.k + row * S::kKStride + 16 * unit) = r.k[i];
-    const int ks = key_slot(row);
-    const int d0 = unit * C::kDimsPerUnit;
-    unsigned w[8];
-    if constexpr (FP8) {
+    uint8_t* kd = st.k + row * S::kKStride;
+    uint8_t* vd = st.v + row * S::kVStride;
+    if constexpr (FP8) {  // 16 codes -> 32 bytes of bf16
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 x = fp8x4_to_bf16(r.v[i][q]);
-        w[2 * q] = x[0];
-        w[2 * q + 1] = x[1];
+      for (int half = 0; half < 2; ++half) {
+        const u32x2 ka = fp8x4_to_bf16(r.k[i][2 * half]), kb2 = fp8x4_to_bf16(r.k[i][2 * half + 1]);
+        const u32x2 va = fp8x4_to_bf16(r.v[i][2 * half]), vb = fp8x4_to_bf16(r.v[i][2 * half + 1]);
+        *reinterpret_cast<u32x4*>(kd + 32 * unit + 16 * half) = u32x4{ka[0], ka[1], kb2[0], kb2[1]};
+        *reinterpret_cast<u32x4*>(vd + 32 * unit + 16 * half) = u32x4{va[0], va[1], vb[0], vb[1]};
       }
     } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = r.v[i][q];
-    }
-    uint8_t* col = st.vt + d0 * S::kVStride + 2 * ks;
-#pragma unroll
-    for (int e = 0; e < C::kDimsPerUnit; ++e) {
-      const unsigned word = w[e >> 1];
-      *reinterpret_cast<uint16_t*>(col + e * S::kVStride) =
-          static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
+      *reinterpret_cast<u32x4*>(kd + 16 * unit) = r.k[i];
+      *reinterpret_cast<u32x4*>(vd + 16 * unit) = r.v[i];
     }
   }
 }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read of four 16-bit values (see the header).
+__device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+__device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]), fmaxf(fmaxf(fmaxf(a[3], b[0]), b[1]),
+                                                     fmaxf(fmaxf(b[2], b[3]), -INFINITY)));
+}
+
+// Online-softmax state of one query row and head: running maximum m (log2 units),
+// -m (0 while m = -inf), the raise threshold m + 8, and this lane's share of the
+// probability sum (the row's four lanes are added at the end).
+struct RowState {
+  float m, negm, raise_at, l;
+};
 
 // One 32-key block for this wave's 16 query tokens and HPW heads (lane (n, gq): query
 // n). diag: the block reaches past some token's position, so keys j > pos are masked.
 // The rare cases (masking, raising the maximum, the low part of P) are uniform
 // branches inside one body, so the accumulators keep one register assignment.
 template <int D, bool FP8, int HPW>
-__device__ __forceinline__ void attend_block(const Stage<D, FP8>& st,
+__device__ __forceinline__ void attend_block(const Stage<D>& st,
                                              const u32x4 (&qf)[HPW][PCfg<D, FP8>::kSteps],
                                              f32x4 (&acc)[HPW][PCfg<D, FP8>::kDimBlocks],
-                                             float (&m)[HPW], float (&l)[HPW], bool diag, int j0,
-                                             int pos, int n, int gq, float c, float v_mul) {
+                                             RowState (&rs)[HPW], bool diag, int j0, int pos, int n,
+                                             int gq, float c, float v_mul) {
   using C = PCfg<D, FP8>;
-  using S = Stage<D, FP8>;
+  using S = Stage<D>;
   // K operands: key 16h + n, dims op_dim(s, gq, 0..7).
   const uint8_t* kbase = st.k + n * S::kKStride + 16 * gq;
   u32x4 kop[2][C::kSteps];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint8_t* krow = kbase + 16 * h * S::kKStride;
-    if constexpr (FP8) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int u = 0; u < C::kSteps / 2; ++u) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(krow + 64 * u);
-        const u32x2 a = fp8x4_to_bf16(x[0]), bq = fp8x4_to_bf16(x[1]);
-        const u32x2 c2 = fp8x4_to_bf16(x[2]), d2 = fp8x4_to_bf16(x[3]);
-        kop[h][2 * u] = u32x4{a[0], a[1], bq[0], bq[1]};
-        kop[h][2 * u + 1] = u32x4{c2[0], c2[1], d2[0], d2[1]};
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) kop[h][s] = *reinterpret_cast<const u32x4*>(krow + 64 * s);
-    }
-  }
+    for (int s = 0; s < C::kSteps; ++s)
+      kop[h][s] = *reinterpret_cast<const u32x4*>(kbase + 16 * h * S::kKStride + 64 * s);
   // Raw scores S^T: lane (n, gq) holds keys j0 + 16h + 4gq + v of query n.
   f32x4 sacc[HPW][2];
 #pragma unroll
@@ -267,46 +285,50 @@ __device__ __forceinline__ void attend_block(const Stage<D, FP8>& st,
         for (int v = 0; v < 4; ++v)
           if (16 * h + v > lim) sacc[hh][h][v] = -INFINITY;
   }
-  // Row maxima of the block (raw units; c > 0 keeps the order).
-  float cmax[HPW];
+  // Block maxima (raw units; c > 0 keeps the order): this lane's, and the row's.
+  float xlane[HPW], cmax[HPW];
   bool raise = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    float x = fmaxf(fmaxf(sacc[hh][0][0], sacc[hh][0][1]), fmaxf(sacc[hh][0][2], sacc[hh][0][3]));
-    x = fmaxf(x, fmaxf(fmaxf(sacc[hh][1][0], sacc[hh][1][1]), fmaxf(sacc[hh][1][2], sacc[hh][1][3])));
-    cmax[hh] = group_max(x);
-    raise |= cmax[hh] * c > m[hh] + kRescaleSlack;
+    xlane[hh] = max8(sacc[hh][0], sacc[hh][1]);
+    cmax[hh] = group_max(xlane[hh]);
+    raise |= cmax[hh] * c > rs[hh].raise_at;
   }
   if (__builtin_amdgcn_ballot_w64(raise)) {
     __asm__ volatile("");  // keeps this rare path a branch (not a select on every block)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const float mc = cmax[hh] * c;
-      const bool up = mc > m[hh] + kRescaleSlack;
-      const float alpha = up ? __builtin_amdgcn_exp2f(m[hh] - mc) : 1.f;  // m = -inf gives 0
+      const bool up = mc > rs[hh].raise_at;
+      const float alpha = up ? __builtin_amdgcn_exp2f(rs[hh].m - mc) : 1.f;  // m = -inf gives 0
 #pragma unroll
       for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] *= alpha;
-      l[hh] *= alpha;
-      m[hh] = up ? mc : m[hh];
+      rs[hh].l *= alpha;
+      if (up) {
+        rs[hh].m = mc;
+        rs[hh].negm = -mc;
+        rs[hh].raise_at = mc + kRescaleSlack;
+      }
     }
   }
-  // Probabilities p = 2^(s c - m) (times the V scale for FP8), the row sums, and P^T
-  // packed to bf16.
+  // Probabilities p = 2^(s c - m) (times the V scale for FP8), this lane's sums, and
+  // P^T packed to bf16. The low-part test uses this lane's largest p and sum: if a
+  // row's largest p exceeds a quarter of the row's sum after the block, the lane that
+  // holds it sees 3 p > (its sum before the block).
   float pv[HPW][8];
   u32x4 ph[HPW];
   bool low = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const float negm = m[hh] == -INFINITY ? 0.f : -m[hh];
-    const float pmax = __builtin_amdgcn_exp2f(fmaf(cmax[hh], c, negm));
-    low |= kLowPartTest * pmax > l[hh];
-    float rs = 0.f;
+    const float negm = rs[hh].negm;
+    low |= kLowPartTest * __builtin_amdgcn_exp2f(fmaf(xlane[hh], c, negm)) > rs[hh].l;
+    float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pv[hh][e] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][e >> 2][e & 3], c, negm));
-      rs += pv[hh][e];
+      sum += pv[hh][e];
     }
-    l[hh] += group_sum(rs);
+    rs[hh].l += sum;
     if constexpr (FP8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[hh][e] *= v_mul;
@@ -314,12 +336,23 @@ __device__ __forceinline__ void attend_block(const Stage<D, FP8>& st,
 #pragma unroll
     for (int e = 0; e < 4; ++e) ph[hh][e] = pack_bf16(pv[hh][2 * e], pv[hh][2 * e + 1]);
   }
-  // V^T operands: dims 16bl + n, keys in operand order.
+  // V^T operands: dims 16bl + n, keys 4gq + 0..3 then 16 + 4gq + 0..3 (two
+  // transposing reads; lane (n, gq) addresses row 4gq + n / 4, dims 16bl + 4 (n % 4)).
+  const uint8_t* vbase = st.v + (4 * gq + (n >> 2)) * S::kVStride + 8 * (n & 3);
   u32x4 vop[C::kDimBlocks];
 #pragma unroll
-  for (int bl = 0; bl < C::kDimBlocks; ++bl)
-    vop[bl] = *reinterpret_cast<const u32x4*>(st.vt + (16 * bl + n) * S::kVStride + 16 * gq);
+  for (int bl = 0; bl < C::kDimBlocks; ++bl) {
+    const u32x2 lo = read_tr16(vbase + 32 * bl);
+    const u32x2 hi = read_tr16(vbase + 16 * S::kVStride + 32 * bl);
+    vop[bl] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = mfma_bf16(vop[bl], ph[hh], acc[hh][bl]);
   if (__builtin_amdgcn_ballot_w64(low)) {
+    // The low part goes through a fresh accumulator and is added in place, so the
+    // accumulators keep their registers whichever way this branch goes.
     __asm__ volatile("");
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -328,13 +361,10 @@ __device__ __forceinline__ void attend_block(const Stage<D, FP8>& st,
       for (int e = 0; e < 4; ++e)
         pl[e] = pack_bf16(pv[hh][2 * e] - bf16_lo(ph[hh][e]), pv[hh][2 * e + 1] - bf16_hi(ph[hh][e]));
 #pragma unroll
-      for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = mfma_bf16(vop[bl], pl, acc[hh][bl]);
+      for (int bl = 0; bl < C::kDimBlocks; ++bl)
+        acc[hh][bl] += mfma_bf16(vop[bl], pl, f32x4{0.f, 0.f, 0.f, 0.f});
     }
   }
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-    for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = mfma_bf16(vop[bl], ph[hh], acc[hh][bl]);
 }
 
 template <int D, bool FP8, int GWI>
@@ -344,7 +374,7 @@ void prefill_kernel(const PrefillParams p) {
   using W = WaveCfg<GWI>;
   constexpr int HPW = W::kHeadsPerWave;
   constexpr int NT = W::kThreads;
-  __shared__ Stage<D, FP8> stage[2];
+  __shared__ Stage<D> stage[2];
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slice = wid & 3, head_pair = wid >> 2;
@@ -362,13 +392,9 @@ void prefill_kernel(const PrefillParams p) {
   const int h0 = g * G + hg * GWI + head_pair * HPW;  // this wave's first query head
   const int first_pos = L - nq;                       // position of query token 0
 
-  TileCtx ctx;
-  ctx.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-  ctx.row_bytes = C::kRowBytes;
-  ctx.head_off = static_cast<int64_t>(g) * p.page_size * C::kRowBytes;
-  ctx.page_bytes = static_cast<int64_t>(p.num_kv_heads) * p.page_size * C::kRowBytes;
-  ctx.L = L;
-  ctx.page_size = p.page_size;
+  const int32_t* __restrict__ bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  const int64_t head_off = static_cast<int64_t>(g) * p.page_size * C::kRowBytes;
+  const int64_t page_bytes = static_cast<int64_t>(p.num_kv_heads) * p.page_size * C::kRowBytes;
 
   // This lane's query token and its causal limit (rows past the request's end reuse
   // the last position and are not written).
@@ -396,50 +422,73 @@ void prefill_kernel(const PrefillParams p) {
     const uint16_t* qrow = p.q + (static_cast<int64_t>(q0 + (valid ? t : 0)) * p.num_q_heads + h0 + hh) * D;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
-      qf[hh][s] = valid ? *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0))
+      qf[hh][s] = valid ? *reinterpret_cast<const u32x4*>(qrow + op_dim(s, gq, 0))
                         : u32x4{0u, 0u, 0u, 0u};
       qf[hh][s] ^= u32x4{qflip, qflip, qflip, qflip};
     }
   }
 
   f32x4 acc[HPW][C::kDimBlocks];
-  float m[HPW], l[HPW];
+  RowState rs[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
     for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
+    rs[hh] = RowState{-INFINITY, 0.f, -INFINITY, 0.f};
   }
 
   // Double-buffered stage: block kb is written into stage[kb & 1] while the other
-  // buffer may still be read; the one barrier per block separates both uses.
-  BlockRegs<D, FP8, NT> regs;
-  load_block<D, FP8, NT>(regs, ctx, p.k_cache, p.v_cache, 0, tid);
+  // buffer may still be read; the one barrier per block separates both uses. The
+  // block-table entries (and FP8 page scales) are loaded one block ahead of the K/V
+  // loads that use them.
+  using R = BlockRegs<D, FP8, NT>;
+  const int last_page = (L - 1) / p.page_size;
+  R regs;
+  walk_init<D, FP8, NT>(regs, p.page_size, tid);
+  block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+  load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, 0, L, tid);
+  if (nblocks > 1) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+  float ksc = 1.f, vsc = 1.f;  // FP8 page scales of the block being computed
+  int scale_page = 0;          // FP8: physical page of the next block
+  if constexpr (FP8) {
+    const int64_t sidx = static_cast<int64_t>(bt[0]) * p.num_kv_heads + g;
+    ksc = p.k_scale[sidx];
+    vsc = p.v_scale[sidx];
+    scale_page = bt[min(kBlockKeys, L - 1) / p.page_size];
+  }
   for (int kb = 0; kb < nblocks; ++kb) {
-    Stage<D, FP8>& st = stage[kb & 1];
+    Stage<D>& st = stage[kb & 1];
     stage_block<D, FP8, NT>(st, regs, tid);
     __syncthreads();
-    if (kb + 1 < nblocks) load_block<D, FP8, NT>(regs, ctx, p.k_cache, p.v_cache, kb + 1, tid);
+    float ksc_next = 1.f, vsc_next = 1.f;
+    if (kb + 1 < nblocks) {
+      load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, kb + 1, L, tid);
+      if (kb + 2 < nblocks) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+      if constexpr (FP8) {
+        const int64_t sidx = static_cast<int64_t>(scale_page) * p.num_kv_heads + g;
+        ksc_next = p.k_scale[sidx];
+        vsc_next = p.v_scale[sidx];
+        if (kb + 2 < nblocks) scale_page = bt[min((kb + 2) * kBlockKeys, L - 1) / p.page_size];
+      }
+    }
     if (kb < wave_blocks) {
       const int j0 = kb * kBlockKeys;
-      float c = qk_log2, v_mul = 1.f;
-      if constexpr (FP8) {
-        const int64_t sidx = static_cast<int64_t>(ctx.bt[j0 / p.page_size]) * p.num_kv_heads + g;
-        c = qk_log2 * p.k_scale[sidx];
-        v_mul = p.v_scale[sidx];
-      }
-      attend_block<D, FP8, HPW>(st, qf, acc, m, l, j0 + kBlockKeys - 1 > wave_first_pos, j0, pos,
-                                n, gq, c, v_mul);
+      attend_block<D, FP8, HPW>(st, qf, acc, rs, j0 + kBlockKeys - 1 > wave_first_pos, j0, pos, n,
+                                gq, qk_log2 * ksc, vsc);
     }
+    ksc = ksc_next;
+    vsc = vsc_next;
   }
 
-  // Rows to the output: lane (n, gq) holds dims 16bl + 4gq + v of query n; l is the
-  // row's fp32 probability sum (the same in the row's four lanes).
+  // Rows to the output: lane (n, gq) holds dims 16bl + 4gq + v of query n; the row's
+  // probability sum is the sum of its four lanes' shares.
+  float lrow[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) lrow[hh] = group_sum(rs[hh].l);
   if (!valid) return;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
+    const float inv = lrow[hh] > 0.f ? 1.f / lrow[hh] : 0.f;
     const int64_t row = static_cast<int64_t>(q0 + t) * p.num_q_heads + h0 + hh;
     uint16_t* orow = p.out + row * D;
 #pragma unroll
@@ -450,7 +499,7 @@ void prefill_kernel(const PrefillParams p) {
       *reinterpret_cast<u32x2*>(orow + d) = w;
     }
     if (p.lse != nullptr && gq == 0)
-      p.lse[row] = l[hh] > 0.f ? (m[hh] + __builtin_amdgcn_logf(l[hh])) * kLn2 : -INFINITY;
+      p.lse[row] = lrow[hh] > 0.f ? (rs[hh].m + __builtin_amdgcn_logf(lrow[hh])) * kLn2 : -INFINITY;
   }
 }
 
