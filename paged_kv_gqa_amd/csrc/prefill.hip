@@ -233,22 +233,25 @@ __device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, x);
 }
 
-__device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
-  return fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]), fmaxf(fmaxf(fmaxf(a[3], b[0]), b[1]),
-                                                     fmaxf(fmaxf(b[2], b[3]), -INFINITY)));
+__device__ __forceinline__ float max8(const float (&a)[8]) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]),
+               fmaxf(fmaxf(fmaxf(a[3], a[4]), a[5]), fmaxf(a[6], a[7])));
 }
 
-// Online-softmax state of one query row and head: running maximum m (log2 units),
-// -m (0 while m = -inf), the raise threshold m + 8, and this lane's share of the
-// probability sum (the row's four lanes are added at the end).
+// Online-softmax state of one query row and head: running maximum m (log2 units;
+// -inf before the first block), negm = -m (+inf before the first block, so that the
+// first block always raises m), and this lane's share of the probability sum (the
+// row's four lanes are added at the end).
 struct RowState {
-  float m, negm, raise_at, l;
+  float m, negm, l;
 };
 
 // One 32-key block for this wave's 16 query tokens and HPW heads (lane (n, gq): query
 // n). diag: the block reaches past some token's position, so keys j > pos are masked.
-// The rare cases (masking, raising the maximum, the low part of P) are uniform
-// branches inside one body, so the accumulators keep one register assignment.
+// Per key the exponent argument a = s c - m is formed first; the row maximum needs a
+// cross-lane reduction only when some lane sees a > 8 (m must be raised), a rare
+// branch. The rare cases (masking, raising the maximum, the low part of P) are
+// uniform branches inside one body, so the accumulators keep one register assignment.
 template <int D, bool FP8, int HPW>
 __device__ __forceinline__ void attend_block(const Stage<D>& st,
                                              const u32x4 (&qf)[HPW][PCfg<D, FP8>::kSteps],
@@ -285,47 +288,52 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
         for (int v = 0; v < 4; ++v)
           if (16 * h + v > lim) sacc[hh][h][v] = -INFINITY;
   }
-  // Block maxima (raw units; c > 0 keeps the order): this lane's, and the row's.
-  float xlane[HPW], cmax[HPW];
+  // Exponent arguments a = s c - m (masked keys: -inf, since c > 0) and their lane max.
+  float arg[HPW][8], amax[HPW];
   bool raise = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    xlane[hh] = max8(sacc[hh][0], sacc[hh][1]);
-    cmax[hh] = group_max(xlane[hh]);
-    raise |= cmax[hh] * c > rs[hh].raise_at;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(sacc[hh][e >> 2][e & 3], c, rs[hh].negm);
+    amax[hh] = max8(arg[hh]);
+    raise |= amax[hh] > kRescaleSlack;
   }
   if (__builtin_amdgcn_ballot_w64(raise)) {
     __asm__ volatile("");  // keeps this rare path a branch (not a select on every block)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      const float mc = cmax[hh] * c;
-      const bool up = mc > rs[hh].raise_at;
-      const float alpha = up ? __builtin_amdgcn_exp2f(rs[hh].m - mc) : 1.f;  // m = -inf gives 0
+      float raw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) raw[e] = sacc[hh][e >> 2][e & 3];
+      const float mc = group_max(max8(raw)) * c;  // the row's block maximum, log2 units
+      // Lanes whose row keeps its maximum multiply by 1 (no divergent branch, so the
+      // accumulators are scaled in place).
+      const bool up = mc > rs[hh].m + kRescaleSlack;  // the same in the row's four lanes
+      const float alpha = up ? __builtin_amdgcn_exp2f(rs[hh].m - mc) : 1.f;  // m = -inf: 0
 #pragma unroll
       for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] *= alpha;
       rs[hh].l *= alpha;
-      if (up) {
-        rs[hh].m = mc;
-        rs[hh].negm = -mc;
-        rs[hh].raise_at = mc + kRescaleSlack;
-      }
+      rs[hh].m = up ? mc : rs[hh].m;
+      rs[hh].negm = up ? -mc : rs[hh].negm;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(raw[e], c, rs[hh].negm);
+      amax[hh] = max8(arg[hh]);
     }
   }
-  // Probabilities p = 2^(s c - m) (times the V scale for FP8), this lane's sums, and
-  // P^T packed to bf16. The low-part test uses this lane's largest p and sum: if a
-  // row's largest p exceeds a quarter of the row's sum after the block, the lane that
-  // holds it sees 3 p > (its sum before the block).
+  // Probabilities p = 2^a (times the V scale for FP8), this lane's sums, and P^T
+  // packed to bf16. The low-part test uses this lane's largest p and sum: if a row's
+  // largest p exceeds a quarter of the row's sum after the block, the lane that holds
+  // it sees 3 p > (its sum before the block).
   float pv[HPW][8];
   u32x4 ph[HPW];
   bool low = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const float negm = rs[hh].negm;
-    low |= kLowPartTest * __builtin_amdgcn_exp2f(fmaf(xlane[hh], c, negm)) > rs[hh].l;
+    low |= kLowPartTest * __builtin_amdgcn_exp2f(amax[hh]) > rs[hh].l;
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pv[hh][e] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][e >> 2][e & 3], c, negm));
+      pv[hh][e] = __builtin_amdgcn_exp2f(arg[hh][e]);
       sum += pv[hh][e];
     }
     rs[hh].l += sum;
@@ -434,7 +442,7 @@ void prefill_kernel(const PrefillParams p) {
   for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
     for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    rs[hh] = RowState{-INFINITY, 0.f, -INFINITY, 0.f};
+    rs[hh] = RowState{-INFINITY, INFINITY, 0.f};
   }
 
   // Double-buffered stage: block kb is written into stage[kb & 1] while the other
@@ -473,8 +481,10 @@ void prefill_kernel(const PrefillParams p) {
     }
     if (kb < wave_blocks) {
       const int j0 = kb * kBlockKeys;
+      // c > 0 keeps masked keys at a = -inf (a zero scale acts as the smallest normal one).
+      const float c = fmaxf(qk_log2 * ksc, 1.17549435e-38f);
       attend_block<D, FP8, HPW>(st, qf, acc, rs, j0 + kBlockKeys - 1 > wave_first_pos, j0, pos, n,
-                                gq, qk_log2 * ksc, vsc);
+                                gq, c, vsc);
     }
     ksc = ksc_next;
     vsc = vsc_next;
