@@ -209,6 +209,55 @@ def prefill_main(args):
     print(json.dumps(rec), flush=True)
 
 
+def percentiles(us):
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def step_distribution(step, dev, n=50, flush_mib=512):
+    """Per-step GPU time of `step` (events on the current stream around the whole step),
+    back to back and with the caches flushed before every step: a fill kernel writes
+    `flush_mib` MiB (twice the 256 MB MALL, far beyond the L2s) outside the events."""
+    import torch
+    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for flush in (False, True):
+        evs = []
+        for i in range(n):
+            if flush:
+                scratch.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        out["flushed" if flush else "back_to_back"] = percentiles([a.elapsed_time(b) * 1e3 for a, b in evs])
+    del scratch
+    return out
+
+
+def host_plan_us(inp, tile_tokens, num_workers, reps=1000):
+    """Median wall time of the host planner (tile choice + plan) over `reps` calls."""
+    import numpy as np
+    import paged_kv_gqa_amd as pkv
+    sl = inp.seq_lens
+    T, N, _ = pkv.pkv_plan_query(sl, inp.q_len, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                                 inp.page_size, inp.kv_format, tile_tokens, num_workers)
+    bufs = (np.empty((N, 4), np.int32), np.empty(num_workers + 1, np.int32),
+            np.empty(inp.batch + 1, np.int32))
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        T, N, _ = pkv.pkv_plan_query(sl, inp.q_len, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                                     inp.page_size, inp.kv_format, tile_tokens, num_workers)
+        pkv.pkv_plan(sl, inp.q_len, inp.num_kv_heads, T, num_workers, out=bufs)
+        times.append((time.perf_counter() - t0) * 1e6)
+    return percentiles(times)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +281,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--no-distribution", action="store_true",
+                    help="skip the per-step time distribution (back to back and cache-flushed)")
+    ap.add_argument("--dist-steps", type=int, default=50)
     ap.add_argument("--prefill", default=None, metavar="WORKLOAD",
                     help="time variable-length causal prefill on a prefill workload "
                          "(prefill_varlen, prefill_long, prefill_chunk_fp8) instead of decode")
@@ -386,6 +438,21 @@ def main():
             "avg_launch_us": round(kern_avg_s * 1e6, 2),
         },
     }
+    if not args.no_distribution:
+        log("step distribution: back to back and flushed, %d steps each" % args.dist_steps)
+        dist = step_distribution(lambda: step(), dev, n=args.dist_steps)
+        dist["host_plan_us"] = None if args.device_plan else host_plan_us(
+            inp, args.tile_tokens, plan["W"])
+        dist["plan_upload_us"] = 0.0 if not args.device_plan else None
+        dist["note"] = ("GPU time per whole step from events on the step's stream; flushed = a "
+                        "512 MiB fill before every step, outside the events. The host plan is "
+                        "written into mapped pinned memory that the kernels read in place, so "
+                        "there is no plan upload." if not args.device_plan else
+                        "GPU time per whole step; the plan is built on the device inside the step.")
+        rec["timing"] = dist
+        log("flushed step median %.1f us (p10 %.1f, p90 %.1f); back to back %.1f us" % (
+            dist["flushed"]["median"], dist["flushed"]["p10"], dist["flushed"]["p90"],
+            dist["back_to_back"]["median"]))
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
