@@ -171,3 +171,27 @@ def test_full_size_sampled_rows(name):
     ref_out, ref_lse = prefill_attention(p, pairs=pairs, rows=sample_rows(p, rng))
     compare(p, out, lse, ref_out, ref_lse, name)
     assert np.isfinite(out).all() and np.isfinite(lse).all()     # every row of every head written
+
+
+def test_empty_requests_are_skipped():
+    """Requests with no query tokens (a prefix only) sit between others; an all-empty
+    batch plans no work and launches nothing."""
+    p = synth.make_prefill_inputs(cfg(), seed=21, q_lens=[0, 5, 0, 70], prefix=[9, 3, 40, 0],
+                                  poison=True, slack_pages=2)
+    out, lse, _ = run_prefill(p)
+    ref_out, ref_lse = prefill_attention(p)
+    compare(p, out, lse, ref_out, ref_lse, "empty_requests")
+    empty = synth.make_prefill_inputs(cfg(), seed=22, q_lens=[0, 0], prefix=[4, 8])
+    out, lse, _ = run_prefill(empty)
+    assert out.shape[0] == 0 and lse.shape[0] == 0
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_negative_and_zero_scale(scale):
+    """A negative softmax scale is taken exactly (Q's sign flipped); a zero scale gives
+    the mean of the visible V rows."""
+    p = synth.make_prefill_inputs(cfg(), seed=23, q_lens=[40, 9], prefix=[30, 0])
+    p.cache.scale = np.float32(scale)
+    out, lse, _ = run_prefill(p)
+    ref_out, ref_lse = prefill_attention(p)
+    compare(p, out, lse, ref_out, ref_lse, "scale_%g" % scale)
