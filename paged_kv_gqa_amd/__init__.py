@@ -1,13 +1,17 @@
-"""Python binding of libpkv.so: paged-KV GQA split-KV decode attention on MI355X.
+"""Python binding of libpkv.so: paged-KV GQA attention on MI355X.
 
 Thin ctypes wrappers with the C ABI's names (argument marshalling only; every step
-of the decode path runs in the library), plus ``PagedDecode``, a per-step runner
-that plans on the host into mapped pinned memory the kernels read in place (or, with
-``device_plan=True``, enqueues the device-side planner) and enqueues the two kernels
-on the caller's stream. PyTorch supplies device memory and streams.
+runs in the library): split-KV decode (host or device plan, partial kernel, combine),
+block-sparse decode, the fused KV append, and variable-length prefill. On top of them:
+- ``PagedDecode``, a per-step runner that plans on the host into mapped pinned memory
+  the kernels read in place (or, with ``device_plan=True``, enqueues the device-side
+  planner) and enqueues the kernels on the caller's stream;
+- ``PagedPrefill``, which plans prefill tiles on the host and enqueues the prefill
+  kernel.
+PyTorch supplies device memory and streams.
 
-The library is built in-tree (``python -m paged_kv_gqa_amd._build``); importing
-this package without it raises ImportError - there is no fallback path.
+The library is built in-tree (``python paged_kv_gqa_amd/_build.py``); importing this
+package without it raises ImportError - there is no fallback path.
 """
 
 import ctypes
@@ -102,7 +106,7 @@ class PrefillArgs(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libpkv.so is not built (expected at %s); run "
-                          "`python -m paged_kv_gqa_amd._build`" % LIB_PATH)
+                          "`python paged_kv_gqa_amd/_build.py` from the repository root" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "pkv_abi_version": (ctypes.c_int, []),

@@ -1,6 +1,9 @@
 """Build libpkv.so in-tree with hipcc for gfx950 (no JIT, no site-packages install).
 
-    python -m paged_kv_gqa_amd._build
+    python paged_kv_gqa_amd/_build.py
+
+(Run as a file: importing it through the package would load the package, which needs
+the library.)
 """
 
 import os
