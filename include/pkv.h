@@ -377,7 +377,11 @@ typedef struct pkv_prefill_args {
  * Enqueue the prefill kernel: one workgroup per work item; for its 64 query tokens and
  * head group it walks the causal key range in 32-key blocks with an online softmax
  * and writes each row's normalised output (bf16) and log-sum-exp. Every row of every
- * request must be covered by the items (pkv_prefill_plan's list). Enqueue only.
+ * request must be covered by the items (pkv_prefill_plan's list). Device contents are
+ * the caller's contract: an item outside the batch, or of a request with
+ * kv_len < n_b or kv_len > bt_stride * P, is skipped and its rows are not written.
+ * The softmax scale may be negative (taken exactly); a zero scale acts as the smallest
+ * normal float. FP8 page scales must be positive. Enqueue only.
  * Errors: INVALID_ARG, UNSUPPORTED (D not 64/128, P not a multiple of 16, fp8 with
  * P != 64, G not 1, 2 or a multiple of 4), ALIGNMENT (q, out, caches, items 16 bytes),
  * HIP.
