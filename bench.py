@@ -5,9 +5,11 @@
 One step = the whole hot path over one decode batch: host plan (uniform tiles,
 greedy bin-packing) written into mapped pinned memory that the kernels read in
 place, the split-KV partial kernel and the log-sum-exp combine kernel, all on one
-stream. Inputs (seeded, synthetic) are
-resident in HBM before timing starts. Prints ONE JSON line on stdout; progress
-goes to stderr.
+stream. Inputs (seeded, synthetic) are resident in HBM before timing starts. After
+an untimed ramp (--ramp-ms of steps, so the GPU's clocks have risen) and W warmup
+steps, exactly K steps are timed by wall clock between synchronisations; the decode
+kernel is timed with HIP events on every --event-every-th of them. Prints ONE JSON
+line on stdout; progress goes to stderr.
 
 value = algorithmic bytes / wall time per step (GB/s). Algorithmic bytes: K and V of
 every valid token, Q, the bf16 output, the block-table entries used, seq_lens and
@@ -73,6 +75,41 @@ def cpu_baseline(inp, algo_bytes):
             "sample": "one full step of the same workload (all %d requests x %d kv heads), "
                       "fp64 numpy, host cores of the GPU box" % (inp.batch, inp.num_kv_heads),
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def ramp(step, ms):
+    """Untimed steps for at least `ms` milliseconds before the warmup steps: the GPU
+    raises its clocks over the first tens of milliseconds of load after idling (input
+    generation), longer than a few warmup steps last. Returns the number of steps."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def timed_steps(step, K, every):
+    """Time exactly K steps (synchronised before and after). The hot kernel is timed with
+    HIP events recorded around its launch on every `every`-th of those steps: each
+    recorded event costs its step GPU time (~3 us), so events on every step would slow
+    the loop they measure. Returns (wall seconds, mean kernel seconds, launches timed)."""
+    import numpy as np
+    import torch
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for i in range(0, K, max(1, every))}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev.values()])) / 1e3
+    return wall, kern, len(ev)
 
 
 PREFILL_METRIC = "causal prefill attention TFLOP/s over the paged KV cache"
@@ -149,19 +186,14 @@ def prefill_main(args):
         if evs is not None:
             evs[1].record()
 
-    log("warmup %d steps" % args.warmup)
+    n_ramp = ramp(step, args.ramp_ms)
+    log("ramp: %d untimed steps; warmup %d steps" % (n_ramp, args.warmup))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     log("timing %d steps" % K)
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    wall, kern_s, n_timed = timed_steps(step, K, args.event_every)
     value = flops / (wall / K) / 1e12
     achieved = flops / kern_s / 1e12
     n_items = int(runner.last_items.shape[0])
@@ -174,6 +206,7 @@ def prefill_main(args):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "ramp_steps": n_ramp,
         "ms_per_step": round(wall / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -202,6 +235,8 @@ def prefill_main(args):
             "traffic": None,
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(kern_s * 1e6, 2),
+            "launches_timed": "%d of the %d timed steps (HIP events on every %d-th)" % (
+                n_timed, K, args.event_every),
         },
     }
     if not args.no_cpu_baseline:
@@ -263,6 +298,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="untimed steps for at least this long before the warmup steps "
+                         "(the GPU's clocks rise over the first tens of ms of load)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="time the hot kernel with HIP events on every N-th timed step")
     ap.add_argument("--workload", default="mixed")
     ap.add_argument("--tile-tokens", type=int, default=0)
     ap.add_argument("--num-workers", type=int, default=0)
@@ -356,7 +396,8 @@ def main():
         runner(q_step, k, v, bt, seq_lens_h, inp.scale, k_scale=ks, v_scale=vs, seq_lens=sl_dev,
                out=out, partial_events=events, block_mask=mask_d, block_mask_h=mask_h)
 
-    log("warmup %d steps" % args.warmup)
+    n_ramp = ramp(step, args.ramp_ms)
+    log("ramp: %d untimed steps; warmup %d steps" % (n_ramp, args.warmup))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -377,16 +418,8 @@ def main():
     log("plan: tile %d tokens, %d items, %d workers" % (plan["T"], plan["N"], plan["W"]))
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     log("timing %d steps" % K)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    wall, kern_avg_s, n_timed = timed_steps(step, K, args.event_every)
     ms_per_step = wall / K * 1e3
     value = algo / (wall / K) / 1e9
     achieved = partial_algo / kern_avg_s / 1e9
@@ -401,6 +434,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "ramp_steps": n_ramp,
         "ms_per_step": round(ms_per_step, 4),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -436,6 +470,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": partial_algo,
             "avg_launch_us": round(kern_avg_s * 1e6, 2),
+            "launches_timed": "%d of the %d timed steps (HIP events on every %d-th)" % (
+                n_timed, K, args.event_every),
         },
     }
     if not args.no_distribution:
