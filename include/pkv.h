@@ -209,7 +209,8 @@ int pkv_plan_device_scratch_bytes(int batch, int num_kv_heads, int page_size, in
  *   info            int32 [4] = {status, T, N, most items on one worker}
  *   scratch         pkv_plan_device_scratch_bytes(...) bytes, 16-byte aligned;
  *                   contents need no initialisation
- * Limits: 1 <= num_workers <= 1024, batch <= 4096, 0 <= max_items <= INT32_MAX / 4.
+ * Limits: 1 <= num_workers <= 1024, batch <= 4096, 0 <= max_items <= INT32_MAX / 4,
+ * tile_tokens <= 262144.
  * Returned errors (nothing enqueued): INVALID_ARG, UNSUPPORTED (shape rules, the
  * limits, tile not a multiple of the quantum), ALIGNMENT, WORKSPACE (scratch too
  * small), HIP. Errors found on the device go to info[0] with an empty plan (every

@@ -306,10 +306,11 @@ int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_hea
     return fail(PKV_ERR_INVALID_ARG, "negative size (batch %d, W %d, T %d, max_items %lld)", batch,
                 num_workers, tile_tokens, static_cast<long long>(max_items));
   if (batch > pkv::kMaxDevicePlanBatch || num_workers > pkv::kMaxDevicePlanWorkers ||
-      max_items > INT32_MAX / 4)
+      max_items > INT32_MAX / 4 || tile_tokens > pkv::kMaxDevicePlanTile)
     return fail(PKV_ERR_UNSUPPORTED, "device plan limits: batch %d (max %d), W %d (max %d), "
-                "max_items %lld", batch, pkv::kMaxDevicePlanBatch, num_workers,
-                pkv::kMaxDevicePlanWorkers, static_cast<long long>(max_items));
+                "max_items %lld, tile_tokens %d (max %d)", batch, pkv::kMaxDevicePlanBatch,
+                num_workers, pkv::kMaxDevicePlanWorkers, static_cast<long long>(max_items),
+                tile_tokens, pkv::kMaxDevicePlanTile);
   const bool fp8 = kv_format == PKV_KV_FP8_E4M3FN;
   const int64_t quantum = pkv::tile_quantum(page_size, fp8);
   if (tile_tokens % quantum != 0)

@@ -102,6 +102,8 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, int he
 // Device planner limits: one thread per worker, the requests sorted in LDS.
 constexpr int kMaxDevicePlanWorkers = 1024;
 constexpr int kMaxDevicePlanBatch = 4096;
+// Largest fixed tile (tokens) a device-built plan takes (its keys are 32-bit).
+constexpr int kMaxDevicePlanTile = 1 << 18;
 // Candidate tiles of the automatic rule: quantum << c, c < num_candidates <= 16.
 constexpr int kMaxDevicePlanCandidates = 16;
 

@@ -20,7 +20,11 @@
 //   4. write the items grouped by worker: full items first, then the worker's
 //      remainder items in placement order.
 // Worker keys live in registers, one per thread, sorted by a bitonic network whose
-// short strides exchange within a wave.
+// short strides exchange within a wave. Keys are 32-bit: a worker's load is kept
+// relative to the current least load, and during step 3 every load lies within T
+// of it (each remainder tile costs less than T and goes to the least-loaded
+// worker, and the full-tile loads differ by at most T), so (relative load, worker)
+// fits in 32 bits for T < 2^18; the reference load is carried beside the keys.
 // Automatic tile size: one workgroup per candidate tile builds that candidate's plan
 // into scratch with its estimate (all candidates at once); a copy kernel then moves
 // the plan with the lowest estimate (ties: the larger tile) into the outputs. The
@@ -41,21 +45,26 @@ constexpr long long kMaxTokenHeads = 1LL << 36;
 constexpr long long kItemBytes = 1LL << 24;
 constexpr int kWorkerRatio = 160;
 
-typedef unsigned long long u64;
+typedef unsigned u32;
 
 static_assert(kMaxDevicePlanWorkers <= kPT && kMaxDevicePlanWorkers <= (1 << kWorkerBits),
               "one thread and one key field per worker");
 static_assert(kMaxDevicePlanBatch <= (1 << kReqBits), "request index field");
+// Remainder-tile key (T - c) << kReqBits | b and worker key (relative load < 2T) <<
+// kWorkerBits | w stay below 2^31, so ~0u is a sentinel above every key.
+static_assert(kMaxDevicePlanTile <= (1 << 18) && 18 + kReqBits <= 31 && 19 + kWorkerBits <= 31,
+              "32-bit keys");
 
 struct PlanLds {
-  u64 rkey[kMaxDevicePlanBatch];        // remainder-tile keys ((T - c) << 13 | b), sorted
+  u32 rkey[kMaxDevicePlanBatch];        // remainder-tile keys ((T - c) << 13 | b), sorted
   int32_t fbx[kMaxDevicePlanBatch];     // exclusive prefix of full items (x Hkv)
   int32_t rtb[kMaxDevicePlanBatch];     // exclusive prefix of n_b
-  u64 xbuf[2][kPT];                     // exchange buffers of the register sort
+  u32 xbuf[2][kPT];                     // exchange buffers of the register sort
   int32_t wcnt[kMaxDevicePlanWorkers];  // remainder items per worker
   int32_t woff[kMaxDevicePlanWorkers];  // first item of each worker
   long long red[5][kWavesP];
-  u64 wmin[kWavesP];
+  u32 wmin[kWavesP];
+  u32 kmin;                             // least worker key after a sort
   int first_miss;                       // first item that breaks the batch
 };
 
@@ -68,8 +77,8 @@ struct PlanOut {
   int2* assign;  // (worker, position in its remainder list) of each remainder item
 };
 
-__device__ __forceinline__ u64 umin(u64 a, u64 b) { return a < b ? a : b; }
-__device__ __forceinline__ u64 umax(u64 a, u64 b) { return a < b ? b : a; }
+__device__ __forceinline__ u32 umin(u32 a, u32 b) { return a < b ? a : b; }
+__device__ __forceinline__ u32 umax(u32 a, u32 b) { return a < b ? b : a; }
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -108,12 +117,6 @@ __device__ __forceinline__ unsigned lane_xor(unsigned v, int j, int lane) {
   }
 }
 
-__device__ __forceinline__ u64 lane_xor64(u64 v, int j, int lane) {
-  const unsigned lo = lane_xor(static_cast<unsigned>(v), j, lane);
-  const unsigned hi = lane_xor(static_cast<unsigned>(v >> 32), j, lane);
-  return (static_cast<u64>(hi) << 32) | lo;
-}
-
 // Ascending bitonic sort of one key per thread: thread t ends with the t-th smallest
 // key of threads 0 .. N-1 (threads >= N hold ~0 and keep it). The network is
 // unrolled, so every stage's stride is a constant: strides below 64 exchange within
@@ -121,7 +124,7 @@ __device__ __forceinline__ u64 lane_xor64(u64 v, int j, int lane) {
 // so one barrier per stage suffices. Callers separate two calls by a workgroup
 // barrier.
 template <int N>
-__device__ __forceinline__ u64 sort_keys_n(u64 x, PlanLds& sm) {
+__device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const bool active = __builtin_amdgcn_readfirstlane(tid) < N;  // wave-uniform
   int buf = 0;
@@ -129,9 +132,9 @@ __device__ __forceinline__ u64 sort_keys_n(u64 x, PlanLds& sm) {
   for (int k = 2; k <= N; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      u64 y = x;
+      u32 y = x;
       if (j < 64) {
-        if (active) y = lane_xor64(x, j, lane);
+        if (active) y = lane_xor(x, j, lane);
       } else {
         if (tid < N) sm.xbuf[buf][tid] = x;
         __syncthreads();
@@ -145,7 +148,7 @@ __device__ __forceinline__ u64 sort_keys_n(u64 x, PlanLds& sm) {
 }
 
 // sort_keys_n for a power of two n <= kPT known at run time.
-__device__ u64 sort_keys(u64 x, int n, PlanLds& sm) {
+__device__ u32 sort_keys(u32 x, int n, PlanLds& sm) {
   switch (n) {
     case 1: return x;
     case 2: return sort_keys_n<2>(x, sm);
@@ -165,13 +168,13 @@ __device__ u64 sort_keys(u64 x, int n, PlanLds& sm) {
 // counts above one key per thread. For strides j <= 64 the pairs of 64 consecutive
 // pair indices stay in one aligned block of 128 elements owned by one wave, so those
 // stages need only wave-level ordering.
-__device__ void lds_sort(u64* s, int n) {
+__device__ void lds_sort(u32* s, int n) {
   const int tid = threadIdx.x;
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int x = tid; x < (n >> 1); x += kPT) {
         const int i = 2 * j * (x / j) + (x & (j - 1));
-        const u64 a = s[i], b = s[i + j];
+        const u32 a = s[i], b = s[i + j];
         if ((a > b) == ((i & k) == 0)) {
           s[i] = b;
           s[i + j] = a;
@@ -266,26 +269,26 @@ __device__ long long block_max(long long v, int nact, PlanLds& sm) {
 
 // Exclusive prefix minimum of v over threads 0 .. n-1 (thread order; ~0 for thread
 // 0 and for threads >= n).
-__device__ u64 block_exclusive_min(u64 v, int n, PlanLds& sm) {
+__device__ u32 block_exclusive_min(u32 v, int n, PlanLds& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const bool active = wid * 64 < n;
-  u64 inc = tid < n ? v : ~0ull;
+  u32 inc = tid < n ? v : ~0u;
   if (active) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const u64 y = __shfl_up(inc, o);
+      const u32 y = __shfl_up(inc, o);
       if (lane >= o) inc = umin(inc, y);
     }
   }
   if (lane == 63) sm.wmin[wid] = inc;
   __syncthreads();
-  u64 pre = ~0ull;
+  u32 pre = ~0u;
   for (int w = 0; w < wid; ++w) pre = umin(pre, sm.wmin[w]);
   if (active) {
-    const u64 prev = __shfl_up(inc, 1);
+    const u32 prev = __shfl_up(inc, 1);
     if (lane > 0) pre = umin(pre, prev);
   }
-  return tid < n ? pre : ~0ull;
+  return tid < n ? pre : ~0u;
 }
 
 __device__ __forceinline__ int pow2_at_least(int x) {
@@ -358,16 +361,16 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
       sm.rtb[b] = pn;
       sm.fbx[b] = pf * Hkv;
       o.req_tile_base[b] = pn;
-      sm.rkey[b] = (c != 0) ? ((static_cast<u64>(uT - c) << kReqBits) | static_cast<u64>(b)) : ~0ull;
+      sm.rkey[b] = (c != 0) ? (((uT - c) << kReqBits) | static_cast<u32>(b)) : ~0u;
       pn += static_cast<int>(f + (c != 0));
       pf += static_cast<int>(f);
     }
-    for (int b = B + tid; b < nB; b += kPT) sm.rkey[b] = ~0ull;
+    for (int b = B + tid; b < nB; b += kPT) sm.rkey[b] = ~0u;
     if (tid == 0) o.req_tile_base[B] = static_cast<int>(tot[0]);
   }
   __syncthreads();
   if (nB <= kPT) {
-    const u64 key = sort_keys(tid < nB ? sm.rkey[tid] : ~0ull, nB, sm);
+    const u32 key = sort_keys(tid < nB ? sm.rkey[tid] : ~0u, nB, sm);
     __syncthreads();
     if (tid < nB) sm.rkey[tid] = key;
   } else {
@@ -375,15 +378,16 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   }
 
   // 2. Loads after the round-robin of the full tiles, already in sorted order:
-  // workers r .. W-1 carry base full tiles, workers 0 .. r-1 one more.
+  // workers r .. W-1 carry base full tiles, workers 0 .. r-1 one more. Keys hold the
+  // load relative to ref = base * T.
   const long long base = F / W;
   const int r = static_cast<int>(F - base * W);
   const int nW = pow2_at_least(W);
-  u64 key = ~0ull;
+  long long ref = base * T;
+  u32 key = ~0u;
   if (tid < W) {
     const int w = (tid < W - r) ? r + tid : tid - (W - r);
-    const long long load = (base + (w < r ? 1 : 0)) * T;
-    key = (static_cast<u64>(load) << kWorkerBits) | static_cast<u64>(w);
+    key = ((w < r ? uT : 0u) << kWorkerBits) | static_cast<u32>(w);
     sm.wcnt[w] = 0;
   }
   __syncthreads();
@@ -394,15 +398,14 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   // least-loaded, lowest-index choice of a one-at-a-time placement).
   for (long long k = 0; k < K;) {
     const int lim = static_cast<int>(min(static_cast<long long>(W), K - k));
-    u64 raised = ~0ull;
-    long long c = 0;
+    u32 raised = ~0u;
     if (tid < lim) {
       const int x = static_cast<int>(k) + tid;
-      c = T - static_cast<long long>(sm.rkey[x / Hkv] >> kReqBits);
-      raised = (((key >> kWorkerBits) + static_cast<u64>(c)) << kWorkerBits) | (key & ((1u << kWorkerBits) - 1));
+      const u32 c = uT - (sm.rkey[x / Hkv] >> kReqBits);  // tokens of the remainder tile
+      raised = key + (c << kWorkerBits);
     }
     if (tid == 0) sm.first_miss = lim;
-    const u64 below = block_exclusive_min(raised, lim, sm);
+    const u32 below = block_exclusive_min(raised, lim, sm);
     if (tid < lim && key > below) atomicMin(&sm.first_miss, tid);
     __syncthreads();
     const int np = sm.first_miss;
@@ -413,7 +416,12 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
       key = raised;
     }
     key = sort_keys(key, nW, sm);
+    if (tid == 0) sm.kmin = key;
     __syncthreads();
+    // Re-base the relative loads on the new least load (every key is at least kmin).
+    const u32 d = sm.kmin >> kWorkerBits;
+    if (tid < W) key -= d << kWorkerBits;
+    ref += d;
     k += np;
   }
 
@@ -421,7 +429,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   // worker, partial bytes.
   long long term = 0, items_w = 0;
   if (tid < W) {
-    const long long l = static_cast<long long>(key >> kWorkerBits);
+    const long long l = ref + static_cast<long long>(key >> kWorkerBits);
     term = (tid <= W - 1 - kWorkerRatio ? l : 0) + (tid == W - 1 ? kWorkerRatio * l : 0);
     items_w = base + (tid < r ? 1 : 0) + sm.wcnt[tid];
   }

@@ -256,6 +256,7 @@ def plan_device_kwargs(**kw):
     (dict(max_items=1 << 30), pkv.PKV_ERR_UNSUPPORTED),
     (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
     (dict(tile_tokens=-16), pkv.PKV_ERR_INVALID_ARG),
+    (dict(tile_tokens=(1 << 18) + 16), pkv.PKV_ERR_UNSUPPORTED),
     (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
     (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),          # fp8 needs page size 64
     (dict(info=None), pkv.PKV_ERR_INVALID_ARG),
