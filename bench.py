@@ -8,8 +8,10 @@ place, the split-KV partial kernel and the log-sum-exp combine kernel, all on on
 stream. Inputs (seeded, synthetic) are resident in HBM before timing starts. After
 an untimed ramp (--ramp-ms of steps, so the GPU's clocks have risen) and W warmup
 steps, exactly K steps are timed by wall clock between synchronisations; the decode
-kernel is timed with HIP events on every --event-every-th of them. Prints ONE JSON
-line on stdout; progress goes to stderr.
+kernel is timed with HIP events on every --event-every-th of them. After the timed
+loop, read probes (libpkv_probe.so) measure this part's own HBM read ceilings, and
+the step is also reported as a percentage of the random 4 KB page gather. Prints ONE
+JSON line on stdout; progress goes to stderr.
 
 value = algorithmic bytes / wall time per step (GB/s). Algorithmic bytes: K and V of
 every valid token, Q, the bf16 output, the block-table entries used, seq_lens and
@@ -75,6 +77,47 @@ def cpu_baseline(inp, algo_bytes):
             "sample": "one full step of the same workload (all %d requests x %d kv heads), "
                       "fp64 numpy, host cores of the GPU box" % (inp.batch, inp.num_kv_heads),
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def read_probe(dev, nbytes=4 << 30, reps=10):
+    """HBM read ceilings of this part, measured by libpkv_probe.so after the timed loop:
+    a contiguous non-temporal stream and a gather of 4 KB pages in random order
+    (decode's access pattern at page size 16), both over a 4 GiB buffer; each the best
+    of three grid sizes (256-thread workgroups). GB/s."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_gqa_amd", "libpkv_probe.so"))
+    vp = ctypes.c_void_p
+    lib.pkvp_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    lib.pkvp_page_gather.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    npages = nbytes // 4096
+    gen = torch.Generator().manual_seed(0)
+    perm = torch.randperm(npages, generator=gen, dtype=torch.int32).to(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
+    def rate(launch):
+        if launch() != 0:
+            raise RuntimeError("read probe launch failed")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        return nbytes / (a.elapsed_time(b) / reps / 1e3) / 1e9
+
+    s = max(rate(lambda: lib.pkvp_stream_read(vp(buf.data_ptr()), nbytes, vp(sink.data_ptr()),
+                                              grid, stream)) for grid in (2048, 8192, 16384))
+    g = max(rate(lambda: lib.pkvp_page_gather(vp(buf.data_ptr()), vp(perm.data_ptr()), npages,
+                                              vp(sink.data_ptr()), grid, stream))
+            for grid in (1024, 2048, 4096))
+    del buf, perm, sink
+    torch.cuda.empty_cache()
+    return s, g
 
 
 def ramp(step, ms):
@@ -321,6 +364,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the HBM read-ceiling probes")
     ap.add_argument("--no-distribution", action="store_true",
                     help="skip the per-step time distribution (back to back and cache-flushed)")
     ap.add_argument("--dist-steps", type=int, default=50)
@@ -489,6 +534,21 @@ def main():
         log("flushed step median %.1f us (p10 %.1f, p90 %.1f); back to back %.1f us" % (
             dist["flushed"]["median"], dist["flushed"]["p10"], dist["flushed"]["p90"],
             dist["back_to_back"]["median"]))
+    if not args.no_read_probe:
+        s_gbs, g_gbs = read_probe(dev)
+        rec["read_probe"] = {
+            "stream_GBs": round(s_gbs, 1),
+            "page_gather_GBs": round(g_gbs, 1),
+            "buffer_GiB": 4,
+            "step_pct_of_page_gather": round(100 * value / g_gbs, 1),
+            "kernel_pct_of_page_gather": round(100 * achieved / g_gbs, 1),
+            "note": "this part's measured read ceilings (libpkv_probe.so, after the timed "
+                    "loop): a contiguous stream and a random 4 KB page gather with "
+                    "non-temporal whole-line loads, the decode kernel's pattern",
+        }
+        log("read probe: stream %.0f GB/s, 4 KB page gather %.0f GB/s; step at %.1f%%, "
+            "decode kernel at %.1f%% of the gather" % (s_gbs, g_gbs, 100 * value / g_gbs,
+                                                       100 * achieved / g_gbs))
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+# Read-bandwidth probes for the bench's roofline (measurement only, a library of its own).
+PROBE_SRC = "read_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
 SOURCES = ["planner.cpp", "api.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip",
            "block_sparse.hip", "kv_append.hip", "prefill.hip"]
@@ -32,7 +35,8 @@ def hipcc():
 
 
 def build(verbose=False):
-    """Compile every source and link libpkv.so; always recompiles."""
+    """Compile every source and link libpkv.so (and the bench's libpkv_probe.so);
+    always recompiles."""
     os.makedirs(OBJ, exist_ok=True)
     objs = []
     for src in SOURCES:
@@ -44,6 +48,12 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
+    probe_obj = os.path.join(OBJ, "read_probe.o")
+    _run([hipcc()] + HIPCC_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, PROBE_SRC), "-o", probe_obj],
+         verbose)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
