@@ -368,7 +368,7 @@ def main():
                     help="skip the HBM read-ceiling probes")
     ap.add_argument("--no-distribution", action="store_true",
                     help="skip the per-step time distribution (back to back and cache-flushed)")
-    ap.add_argument("--dist-steps", type=int, default=50)
+    ap.add_argument("--dist-steps", type=int, default=100)
     ap.add_argument("--prefill", default=None, metavar="WORKLOAD",
                     help="time variable-length causal prefill on a prefill workload "
                          "(prefill_varlen, prefill_long, prefill_chunk_fp8) instead of decode")
@@ -530,6 +530,8 @@ def main():
                         "written into mapped pinned memory that the kernels read in place, so "
                         "there is no plan upload." if not args.device_plan else
                         "GPU time per whole step; the plan is built on the device inside the step.")
+        for kind in ("back_to_back", "flushed"):
+            dist[kind]["GBs_at_median"] = round(algo / (dist[kind]["median"] * 1e-6) / 1e9, 1)
         rec["timing"] = dist
         log("flushed step median %.1f us (p10 %.1f, p90 %.1f); back to back %.1f us" % (
             dist["flushed"]["median"], dist["flushed"]["p10"], dist["flushed"]["p90"],
