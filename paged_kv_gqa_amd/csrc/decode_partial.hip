@@ -123,8 +123,11 @@ struct ItemCtx {
 
 // Byte offsets of the two 16-token halves of a chunk (wave-uniform; the block-table
 // reads are scalar loads). A half past the tile end re-reads half 0 (masked later).
+// phys0: physical page of half 0, which holds the whole chunk when pages are 64
+// tokens (fp8), so it also indexes the chunk's page scales.
 struct HalfOffsets {
   int64_t off[2];
+  int64_t phys0;
 };
 
 __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chunk) {
@@ -136,6 +139,7 @@ __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chun
     if (jh >= it.tile_end) jh = j0;
     const int page = jh / it.page_size;
     const int64_t phys = it.bt[page];
+    if (h == 0) r.phys0 = phys;
     r.off[h] = phys * it.page_bytes + it.head_off +
                static_cast<int64_t>(jh - page * it.page_size) * it.row_bytes;
   }
@@ -381,6 +385,9 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   // while the previous item is still being computed and merged.
   Raw<D, FP8> raw;
   u32x4 qf_next[C::kSteps];
+  // FP8: the K and V page scales of the unit in flight, loaded with its K/V so that
+  // their dependent loads (block-table entry, then scale) stay off the compute path.
+  float ksc_next = 1.f, vsc_next = 1.f;
   int u_itx = -1, u_c = 0;
   ItemInfo u_info;
   auto find_unit = [&](int from) {  // first unit of this wave in items >= from
@@ -397,7 +404,13 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   };
   auto issue_unit = [&]() {
     if (u_itx < 0) return;
-    load_raw<D, FP8>(raw, k_cache, v_cache, chunk_offsets(u_info.it, u_c), lane);
+    const HalfOffsets ho = chunk_offsets(u_info.it, u_c);
+    load_raw<D, FP8>(raw, k_cache, v_cache, ho, lane);
+    if constexpr (FP8) {
+      const int64_t sidx = ho.phys0 * sh.num_kv_heads + u_info.g;
+      ksc_next = k_scale[sidx];
+      vsc_next = v_scale[sidx];
+    }
     if (u_c == wid) {  // first chunk of an item: fetch that item's query fragment
       if (n < M) {
         const int t = n / G;
@@ -439,18 +452,16 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
     while (u_itx == itx) {
       const int c = u_c;
       stage_write<D, FP8>(my_stage, raw, lane);
+      float c_qk = sh.qk_scale_log2, v_mul = 1.f;
+      if constexpr (FP8) {  // this unit's scales, before issue_unit loads the next's
+        c_qk = sh.qk_scale_log2 * ksc_next;
+        v_mul = vsc_next;
+      }
       if (c + kWaves < cur.nchunks)
         u_c = c + kWaves;
       else
         find_unit(itx + 1);
       issue_unit();
-      float c_qk = sh.qk_scale_log2, v_mul = 1.f;
-      if constexpr (FP8) {
-        const int j0 = cur.it.tile_start + 32 * c;
-        const int64_t sidx = static_cast<int64_t>(cur.it.bt[j0 / cur.it.page_size]) * sh.num_kv_heads + cur.g;
-        c_qk = sh.qk_scale_log2 * k_scale[sidx];
-        v_mul = v_scale[sidx];
-      }
       u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
       stage_read<D, FP8>(my_stage, kop, vop, n, gq);
       process_chunk<D, FP8>(kop, vop, qf, sel, acc, m, lsum, lexact, cur.it.tile_start + 32 * c, lim,
