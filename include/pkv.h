@@ -28,6 +28,15 @@
  * - Functions return a pkv_status (0 = success). Nothing aborts or throws across
  *   the ABI. Device entry points validate their host-visible arguments before any
  *   HIP call, then enqueue asynchronously and return without synchronising.
+ * - The contents of device memory (lengths, block-table entries, work lists) are
+ *   the caller's contract and are not read on the host. With the environment
+ *   variable PKV_VALIDATE set (non-empty, not "0"), pkv_decode_partial,
+ *   pkv_combine(_split), pkv_prefill, pkv_kv_append and pkv_block_sparse_compact
+ *   first wait for their stream, copy those arrays to the host and check them, and
+ *   return SEQ (a length below its minimum) or INVALID_ARG (a length past the block
+ *   table, a block-table entry outside [0, num_pages), a work list that is not a
+ *   plan of these lengths) with the detail in pkv_last_error, enqueuing nothing. A
+ *   debugging aid: every such call is synchronous.
  * - Symbols used below: B = requests, Tq = query tokens per request (q_len),
  *   Hq / Hkv = query / kv heads, G = Hq / Hkv, M = G * Tq rows per work item,
  *   D = head_dim, P = page_size, T = tile tokens, W = workers.

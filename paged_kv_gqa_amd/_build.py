@@ -19,9 +19,9 @@ LIB = os.path.join(PKG, "libpkv.so")
 PROBE_SRC = "read_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
-SOURCES = ["planner.cpp", "api.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip",
+SOURCES = ["planner.cpp", "api.cpp", "validate.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip",
            "block_sparse.hip", "kv_append.hip", "prefill.hip"]
-HEADERS = ["planner.hpp", "kernels.hpp"]
+HEADERS = ["planner.hpp", "kernels.hpp", "status.hpp", "validate.hpp"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -16,12 +16,16 @@
 
 #include "kernels.hpp"
 #include "planner.hpp"
+#include "status.hpp"
+#include "validate.hpp"
 
 namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char* fmt, ...) {
+}  // namespace
+
+int pkv::fail(int status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -30,6 +34,10 @@ int fail(int status, const char* fmt, ...) {
   g_last_error = buf;
   return status;
 }
+
+namespace {
+
+using pkv::fail;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -247,6 +255,10 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   p.tile_tokens_dev = tile_dev;
   p.request_split = split;
   p.qk_scale_log2 = a->scale * kLog2e;
+  if (pkv::validate_enabled()) {
+    st = pkv::validate_decode(a, tile_dev, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+  }
   const hipError_t e = pkv::launch_decode_partial(p, a->head_dim, fp8, a->num_workers,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_partial launch: %s", hipGetErrorString(e));
@@ -391,6 +403,11 @@ int pkv_block_sparse_compact(const int32_t* block_table, const int32_t* seq_lens
   p.page_size = page_size;
   p.bt_stride = bt_stride;
   p.mask_stride = mask_stride;
+  if (pkv::validate_enabled()) {
+    const int vst = pkv::validate_block_sparse(block_table, seq_lens, batch, page_size, bt_stride,
+                                               num_pages, static_cast<hipStream_t>(stream));
+    if (vst != PKV_OK) return vst;
+  }
   const hipError_t e = pkv::launch_block_sparse_compact(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "block_sparse_compact launch: %s", hipGetErrorString(e));
   return PKV_OK;
@@ -481,6 +498,10 @@ int pkv_kv_append(const pkv_kv_append_args* a, void* stream) {
   p.page_size = a->page_size;
   p.bt_stride = a->bt_stride;
   p.fp8 = fp8;
+  if (pkv::validate_enabled()) {
+    const int vst = pkv::validate_kv_append(a, static_cast<hipStream_t>(stream));
+    if (vst != PKV_OK) return vst;
+  }
   const hipError_t e = pkv::launch_kv_append(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
   return PKV_OK;
@@ -604,6 +625,11 @@ int pkv_prefill(const pkv_prefill_args* a, void* stream) {
   p.page_size = a->page_size;
   p.bt_stride = a->bt_stride;
   p.scale = a->scale;
+  if (pkv::validate_enabled()) {
+    st = pkv::validate_prefill(a, prefill_heads_per_item(a->num_q_heads, a->num_kv_heads),
+                               static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+  }
   const hipError_t e = pkv::launch_prefill(p, a->head_dim, fp8,
                                            prefill_heads_per_item(a->num_q_heads, a->num_kv_heads),
                                            static_cast<hipStream_t>(stream));
@@ -664,6 +690,11 @@ int pkv_combine_split(const void* workspace, size_t workspace_bytes, int64_t num
   p.group = num_q_heads / num_kv_heads;
   p.rows = rows;
   p.request_split = request_split;
+  if (pkv::validate_enabled()) {
+    const int vst = pkv::validate_combine(req_tile_base, batch, num_kv_heads, num_partials,
+                                          static_cast<hipStream_t>(stream));
+    if (vst != PKV_OK) return vst;
+  }
   const hipError_t e = pkv::launch_combine(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   return PKV_OK;
