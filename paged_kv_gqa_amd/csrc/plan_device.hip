@@ -37,8 +37,10 @@
 namespace pkv {
 namespace {
 
-constexpr int kPT = 1024;                 // threads of a planner workgroup
-constexpr int kWavesP = kPT / 64;
+// Threads of a planner workgroup: one per worker (and per request for the register
+// sort of the request keys), so 512 when W and B allow it, else 1024.
+constexpr int kPT = 1024;
+constexpr int kPTSmall = 512;
 constexpr int kWorkerBits = 10;           // worker index in the low bits of a key
 constexpr int kReqBits = 13;              // request index in the low bits of a key
 constexpr long long kMaxTokenHeads = 1LL << 36;
@@ -49,21 +51,23 @@ typedef unsigned u32;
 
 static_assert(kMaxDevicePlanWorkers <= kPT && kMaxDevicePlanWorkers <= (1 << kWorkerBits),
               "one thread and one key field per worker");
+static_assert(kPTSmall % 64 == 0 && kPTSmall <= kPT, "planner workgroup sizes");
 static_assert(kMaxDevicePlanBatch <= (1 << kReqBits), "request index field");
 // Remainder-tile key (T - c) << kReqBits | b and worker key (relative load < 2T) <<
 // kWorkerBits | w stay below 2^31, so ~0u is a sentinel above every key.
 static_assert(kMaxDevicePlanTile <= (1 << 18) && 18 + kReqBits <= 31 && 19 + kWorkerBits <= 31,
               "32-bit keys");
 
+template <int NT>
 struct PlanLds {
   u32 rkey[kMaxDevicePlanBatch];        // remainder-tile keys ((T - c) << 13 | b), sorted
   int32_t fbx[kMaxDevicePlanBatch];     // exclusive prefix of full items (x Hkv)
   int32_t rtb[kMaxDevicePlanBatch];     // exclusive prefix of n_b
-  u32 xbuf[2][kPT];                     // exchange buffers of the register sort
+  u32 xbuf[2][NT];                      // exchange buffers of the register sort
   int32_t wcnt[kMaxDevicePlanWorkers];  // remainder items per worker
   int32_t woff[kMaxDevicePlanWorkers];  // first item of each worker
-  long long red[5][kWavesP];
-  u32 wmin[kWavesP];
+  long long red[5][NT / 64];
+  u32 wmin[NT / 64];
   u32 kmin;                             // least worker key after a sort
   int first_miss;                       // first item that breaks the batch
 };
@@ -123,8 +127,8 @@ __device__ __forceinline__ unsigned lane_xor(unsigned v, int j, int lane) {
 // a wave (waves past N sit out), wider ones go through LDS, alternating two buffers
 // so one barrier per stage suffices. Callers separate two calls by a workgroup
 // barrier.
-template <int N>
-__device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds& sm) {
+template <int N, int NT>
+__device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds<NT>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const bool active = __builtin_amdgcn_readfirstlane(tid) < N;  // wave-uniform
   int buf = 0;
@@ -147,8 +151,9 @@ __device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds& sm) {
   return x;
 }
 
-// sort_keys_n for a power of two n <= kPT known at run time.
-__device__ u32 sort_keys(u32 x, int n, PlanLds& sm) {
+// sort_keys_n for a power of two n <= NT known at run time.
+template <int NT>
+__device__ u32 sort_keys(u32 x, int n, PlanLds<NT>& sm) {
   switch (n) {
     case 1: return x;
     case 2: return sort_keys_n<2>(x, sm);
@@ -160,19 +165,20 @@ __device__ u32 sort_keys(u32 x, int n, PlanLds& sm) {
     case 128: return sort_keys_n<128>(x, sm);
     case 256: return sort_keys_n<256>(x, sm);
     case 512: return sort_keys_n<512>(x, sm);
-    default: return sort_keys_n<kPT>(x, sm);
+    default: return sort_keys_n<NT>(x, sm);
   }
 }
 
-// Ascending bitonic sort of s[0, n) in LDS (n a power of two <= 4 * kPT) for request
-// counts above one key per thread. For strides j <= 64 the pairs of 64 consecutive
+// Ascending bitonic sort of s[0, n) in LDS (n a power of two) for request counts
+// above one key per thread. For strides j <= 64 the pairs of 64 consecutive
 // pair indices stay in one aligned block of 128 elements owned by one wave, so those
 // stages need only wave-level ordering.
+template <int NT>
 __device__ void lds_sort(u32* s, int n) {
   const int tid = threadIdx.x;
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int x = tid; x < (n >> 1); x += kPT) {
+      for (int x = tid; x < (n >> 1); x += NT) {
         const int i = 2 * j * (x / j) + (x & (j - 1));
         const u32 a = s[i], b = s[i + j];
         if ((a > b) == ((i & k) == 0)) {
@@ -192,8 +198,9 @@ __device__ void lds_sort(u32* s, int n) {
 
 // Exclusive prefix sums (in thread order) of a[0] and a[1] into pre; the workgroup
 // totals of all five values into tot. Waves from `nact` threads on hold zeros.
+template <int NT>
 __device__ void block_scan5(const long long (&a)[5], long long (&pre)[2], long long (&tot)[5],
-                            int nact, PlanLds& sm) {
+                            int nact, PlanLds<NT>& sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   long long inc[5];
 #pragma unroll
@@ -216,7 +223,7 @@ __device__ void block_scan5(const long long (&a)[5], long long (&pre)[2], long l
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     long long base = 0, t = 0;
-    for (int w = 0; w < kWavesP; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
       const long long v = sm.red[i][w];
       base += (w < wid) ? v : 0;
       t += v;
@@ -229,7 +236,8 @@ __device__ void block_scan5(const long long (&a)[5], long long (&pre)[2], long l
 
 // Exclusive prefix sum of v (thread order); *total = workgroup sum. Waves from
 // `nact` threads on hold zeros.
-__device__ long long block_scan(long long v, int nact, PlanLds& sm, long long* total) {
+template <int NT>
+__device__ long long block_scan(long long v, int nact, PlanLds<NT>& sm, long long* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   long long inc = v;
   if (wid * 64 < nact) {
@@ -242,7 +250,7 @@ __device__ long long block_scan(long long v, int nact, PlanLds& sm, long long* t
   if (lane == 63) sm.red[0][wid] = inc;
   __syncthreads();
   long long base = 0, t = 0;
-  for (int w = 0; w < kWavesP; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const long long s = sm.red[0][w];
     base += (w < wid) ? s : 0;
     t += s;
@@ -253,7 +261,8 @@ __device__ long long block_scan(long long v, int nact, PlanLds& sm, long long* t
 }
 
 // Workgroup maximum of v >= 0; waves from `nact` threads on hold zeros.
-__device__ long long block_max(long long v, int nact, PlanLds& sm) {
+template <int NT>
+__device__ long long block_max(long long v, int nact, PlanLds<NT>& sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (wid * 64 < nact) {
 #pragma unroll
@@ -262,14 +271,15 @@ __device__ long long block_max(long long v, int nact, PlanLds& sm) {
   if (lane == 0) sm.red[0][wid] = v;
   __syncthreads();
   long long m = sm.red[0][0];
-  for (int w = 1; w < kWavesP; ++w) m = max(m, sm.red[0][w]);
+  for (int w = 1; w < NT / 64; ++w) m = max(m, sm.red[0][w]);
   __syncthreads();
   return m;
 }
 
 // Exclusive prefix minimum of v over threads 0 .. n-1 (thread order; ~0 for thread
 // 0 and for threads >= n).
-__device__ u32 block_exclusive_min(u32 v, int n, PlanLds& sm) {
+template <int NT>
+__device__ u32 block_exclusive_min(u32 v, int n, PlanLds<NT>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const bool active = wid * 64 < n;
   u32 inc = tid < n ? v : ~0u;
@@ -297,11 +307,12 @@ __device__ __forceinline__ int pow2_at_least(int x) {
   return n;
 }
 
+template <int NT>
 __device__ void write_empty_plan(const DevicePlanParams& p, const PlanOut& o, int status,
                                  long long T) {
   const int tid = threadIdx.x;
-  for (int w = tid; w <= p.num_workers; w += kPT) o.worker_offsets[w] = 0;
-  for (int b = tid; b <= p.batch; b += kPT) o.req_tile_base[b] = 0;
+  for (int w = tid; w <= p.num_workers; w += NT) o.worker_offsets[w] = 0;
+  for (int b = tid; b <= p.batch; b += NT) o.req_tile_base[b] = 0;
   if (tid == 0) {
     o.info[0] = status;
     o.info[1] = static_cast<int>(T);
@@ -312,7 +323,8 @@ __device__ void write_empty_plan(const DevicePlanParams& p, const PlanOut& o, in
 
 // Steps 1-4 for tile size T into `o`. Returns the status (uniform) and, when it is
 // PKV_DEV_OK, the automatic rule's estimate in *est.
-__device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, const PlanOut& o,
+template <int NT>
+__device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& sm, const PlanOut& o,
                           long long* est) {
   const int tid = threadIdx.x;
   const int B = p.batch, Hkv = p.num_kv_heads, W = p.num_workers;
@@ -320,7 +332,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   const unsigned uT = static_cast<unsigned>(T);
 
   // 1. Per-request counts over a contiguous segment per thread.
-  const int per = (B + kPT - 1) / kPT;
+  const int per = (B + NT - 1) / NT;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   long long a[5] = {0, 0, 0, 0, 0};  // tiles, full tiles, tokens, bad lengths, remainders
   for (int b = b0; b < b1; ++b) {
@@ -347,7 +359,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   else if (N > p.max_items)
     status = PKV_DEV_ERR_WORKSPACE;
   if (status != PKV_DEV_OK) {
-    write_empty_plan(p, o, status, T);
+    write_empty_plan<NT>(p, o, status, T);
     return status;
   }
 
@@ -365,16 +377,16 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
       pn += static_cast<int>(f + (c != 0));
       pf += static_cast<int>(f);
     }
-    for (int b = B + tid; b < nB; b += kPT) sm.rkey[b] = ~0u;
+    for (int b = B + tid; b < nB; b += NT) sm.rkey[b] = ~0u;
     if (tid == 0) o.req_tile_base[B] = static_cast<int>(tot[0]);
   }
   __syncthreads();
-  if (nB <= kPT) {
+  if (nB <= NT) {
     const u32 key = sort_keys(tid < nB ? sm.rkey[tid] : ~0u, nB, sm);
     __syncthreads();
     if (tid < nB) sm.rkey[tid] = key;
   } else {
-    lds_sort(sm.rkey, nB);
+    lds_sort<NT>(sm.rkey, nB);
   }
 
   // 2. Loads after the round-robin of the full tiles, already in sorted order:
@@ -454,7 +466,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   int4* items = reinterpret_cast<int4*>(o.items);
   // Full items: the x-th goes to worker x mod W at position x / W.
   const int nF = static_cast<int>(F);
-  for (int x = tid; x < nF; x += kPT) {
+  for (int x = tid; x < nF; x += NT) {
     int lo = 0, hi = B - 1;  // last b with fbx[b] <= x
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -476,7 +488,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds& sm, c
   // Remainder items, in placement order after the worker's full items. The
   // placements were written by this workgroup before the barriers above.
   const int nK = static_cast<int>(K);
-  for (int x = tid; x < nK; x += kPT) {
+  for (int x = tid; x < nK; x += NT) {
     const int qv = x / Hkv;
     const int g = x - qv * Hkv;
     const int b = static_cast<int>(sm.rkey[qv] & ((1u << kReqBits) - 1));
@@ -506,8 +518,9 @@ __device__ PlanOut candidate_out(const DevicePlanParams& p, int c) {
 }
 
 // Automatic tile: workgroup c builds the plan of tile quantum << c into scratch.
-__global__ __launch_bounds__(kPT) void plan_candidates_kernel(const DevicePlanParams p) {
-  __shared__ PlanLds sm;
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_candidates_kernel(const DevicePlanParams p) {
+  __shared__ PlanLds<NT> sm;
   const int c = blockIdx.x;
   long long est = 0;
   const int st = build_plan(p, static_cast<long long>(p.quantum) << c, sm, candidate_out(p, c), &est);
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(kPT) void plan_select_kernel(const DevicePlanParams
     if (blockIdx.x == 0) {
       const int last = p.num_candidates - 1;
       const PlanOut o = {p.items, p.worker_offsets, p.req_tile_base, p.info, nullptr};
-      write_empty_plan(p, o, p.cand_status[last], static_cast<long long>(p.quantum) << last);
+      write_empty_plan<kPT>(p, o, p.cand_status[last], static_cast<long long>(p.quantum) << last);
     }
     return;
   }
@@ -552,8 +565,9 @@ __global__ __launch_bounds__(kPT) void plan_select_kernel(const DevicePlanParams
 }
 
 // Fixed tile: one workgroup builds the plan straight into the outputs.
-__global__ __launch_bounds__(kPT) void plan_fixed_kernel(const DevicePlanParams p) {
-  __shared__ PlanLds sm;
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_fixed_kernel(const DevicePlanParams p) {
+  __shared__ PlanLds<NT> sm;
   const PlanOut o = {p.items, p.worker_offsets, p.req_tile_base, p.info, p.scratch_assign};
   long long est;
   build_plan(p, p.tile_tokens, sm, o, &est);
@@ -562,13 +576,21 @@ __global__ __launch_bounds__(kPT) void plan_fixed_kernel(const DevicePlanParams 
 }  // namespace
 
 hipError_t launch_plan_device(const DevicePlanParams& p, hipStream_t stream) {
+  const bool small = p.num_workers <= kPTSmall && p.batch <= kPTSmall;
   if (p.tile_tokens == 0) {
-    hipLaunchKernelGGL(plan_candidates_kernel, dim3(p.num_candidates), dim3(kPT), 0, stream, p);
+    if (small)
+      hipLaunchKernelGGL(plan_candidates_kernel<kPTSmall>, dim3(p.num_candidates), dim3(kPTSmall), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL(plan_candidates_kernel<kPT>, dim3(p.num_candidates), dim3(kPT), 0, stream, p);
     const long long blocks = (p.max_items + kPT - 1) / kPT;
     const int grid = static_cast<int>(blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks));
     hipLaunchKernelGGL(plan_select_kernel, dim3(grid), dim3(kPT), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(plan_fixed_kernel, dim3(1), dim3(kPT), 0, stream, p);
+    if (small)
+      hipLaunchKernelGGL(plan_fixed_kernel<kPTSmall>, dim3(1), dim3(kPTSmall), 0, stream, p);
+    else
+      hipLaunchKernelGGL(plan_fixed_kernel<kPT>, dim3(1), dim3(kPT), 0, stream, p);
   }
   return hipGetLastError();
 }
