@@ -374,7 +374,7 @@ def main():
                          "(prefill_varlen, prefill_long, prefill_chunk_fp8) instead of decode")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.prefill is not None:
