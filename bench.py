@@ -75,7 +75,7 @@ def cpu_baseline(inp, algo_bytes):
     return {"value": round(algo_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": "one full step of the same workload (all %d requests x %d kv heads), "
-                      "fp64 numpy, host cores of the GPU box" % (inp.batch, inp.num_kv_heads),
+                      "fp64 numpy, on this host's cores" % (inp.batch, inp.num_kv_heads),
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
