@@ -81,6 +81,21 @@ def test_workloads_match_oracle(name, W):
         assert_matches_oracle(sl, *args, Tf, W, n_items, tag="%s T%d W%d" % (name, Tf, W))
 
 
+@pytest.mark.parametrize("B,W", [(300, 500), (600, 256), (1500, 512), (4096, 1024)])
+def test_large_batches_match_oracle(B, W):
+    """Request counts past one key per thread: 512-thread workgroups (W and B at most
+    512), 1024-thread ones with the register sort of the request keys (B <= 1024), and
+    with the LDS sort (B > 1024, up to the 4096 limit)."""
+    rng = np.random.default_rng(B + W)
+    sl = [int(x) for x in np.maximum(np.exp(rng.uniform(0, np.log(3000), B)).astype(int), 1)]
+    Hkv = 2
+    cap = max_candidate_items(sl, Hkv, "bf16", 16)
+    T, N = assert_matches_oracle(sl, 1, 8, Hkv, 128, 16, "bf16", 0, W, cap, tag="B%d W%d auto" % (B, W))
+    log("  B=%d W=%d: auto T=%d N=%d" % (B, W, T, N))
+    n_items = Hkv * sum((L + 63) // 64 for L in sl)
+    assert_matches_oracle(sl, 1, 8, Hkv, 128, 16, "bf16", 64, W, n_items, tag="B%d W%d T64" % (B, W))
+
+
 def test_random_shapes_match_oracle():
     rng = np.random.default_rng(2024)
     for case in range(150):
