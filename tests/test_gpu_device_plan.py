@@ -96,6 +96,16 @@ def test_large_batches_match_oracle(B, W):
     assert_matches_oracle(sl, 1, 8, Hkv, 128, 16, "bf16", 64, W, n_items, tag="B%d W%d T64" % (B, W))
 
 
+def test_page_size_48_matches_oracle():
+    """A page size that is not a power of two: quantum 48, candidates 48 .. 49152."""
+    rng = np.random.default_rng(48)
+    sl = [int(x) for x in rng.integers(1, 5000, 40)]
+    cap = max_candidate_items(sl, 4, "bf16", 48)
+    assert_matches_oracle(sl, 1, 16, 4, 128, 48, "bf16", 0, 333, cap, tag="P48 auto")
+    n_items = 4 * sum((L + 143) // 144 for L in sl)
+    assert_matches_oracle(sl, 1, 16, 4, 128, 48, "bf16", 144, 64, n_items, tag="P48 T144")
+
+
 def test_random_shapes_match_oracle():
     rng = np.random.default_rng(2024)
     for case in range(150):
