@@ -87,6 +87,7 @@ CASES = [
     dict(id="bf16_p16_t1", c=cfg(), rope=False),
     dict(id="bf16_p16_t4_rope", c=cfg(q_len=4), rope=True),
     dict(id="bf16_p32_d64_t3_rope", c=cfg(q_len=3, page_size=32, head_dim=64, num_q_heads=8, num_kv_heads=8), rope=True),
+    dict(id="bf16_p48_t4_rope", c=cfg(q_len=4, page_size=48), rope=True),
     dict(id="fp8_t1", c=cfg(kv_format="fp8", page_size=64), rope=False),
     dict(id="fp8_t2_rope", c=cfg(kv_format="fp8", page_size=64, q_len=2), rope=True),
     dict(id="fp8_t4_rope_g4", c=cfg(kv_format="fp8", page_size=64, q_len=4, num_q_heads=16, num_kv_heads=4), rope=True),
