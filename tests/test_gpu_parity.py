@@ -130,6 +130,67 @@ def test_full_size_workloads_sampled(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_million_token_request(fmt):
+    """One request of 1 000 003 tokens beside a short one (two draft tokens each): tile
+    indices up to 1M / T, host and device plans; every row is checked against the
+    oracle."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    c = cfg(name="long1m", q_len=2, num_q_heads=4, num_kv_heads=1, kv_format=fmt,
+            page_size=64 if fmt == "fp8" else 16)
+    inp = synth.make_inputs(c, seed=41, seq_lens=[1_000_003, 17])
+    log("million-token request %s: %d pages" % (fmt, inp.k_cache.shape[0]))
+    dev = device_inputs(inp)
+    out, lse, bits = run_decode(inp, dev=dev)
+    check(inp, out, lse, tag="1M %s host plan" % fmt)
+    r = pkv.PagedDecode(num_q_heads=4, num_kv_heads=1, head_dim=128, page_size=inp.page_size,
+                        kv_format=fmt, q_len=2, device_plan=True)
+    out_d, lse_d, bits_d = run_decode(inp, dev=dev, runner=r)
+    assert r.plan_info()["status"] == 0
+    assert np.array_equal(bits, bits_d) and np.array_equal(lse, lse_d)
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_pages_past_two_gib(fmt):
+    """The same pages moved to physical indices whose byte offsets lie past 2^31 in a
+    2.4 GB cache (the rest of it NaN, never read): bit-identical to the compact cache."""
+    import torch
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2)
+    inp = synth.make_inputs(c, seed=43, seq_lens=[2, 300, 1000, 5000])
+    dev = device_inputs(inp)
+    _, lse_a, bits_a = run_decode(inp, dev=dev)
+    page_bytes = inp.num_kv_heads * inp.page_size * inp.head_dim * (1 if fmt == "fp8" else 2)
+    base = (1 << 31) // page_bytes + 7                 # first page past 2 GiB, plus some
+    n = inp.k_cache.shape[0]
+    big = {}
+    for name in ("k", "v"):
+        t = torch.full((base + n,) + tuple(dev[name].shape[1:]), float("nan") if fmt == "bf16" else 0,
+                       dtype=dev[name].dtype, device="cuda")
+        if fmt == "fp8":
+            t.fill_(0x7F)                              # e4m3fn NaN
+        t[base:] = dev[name]
+        big[name] = t
+    moved = dict(dev)
+    moved["k"], moved["v"] = big["k"], big["v"]
+    if fmt == "fp8":
+        for name in ("ks", "vs"):
+            t = torch.full((base + n,) + tuple(dev[name].shape[1:]), float("nan"), device="cuda")
+            t[base:] = dev[name]
+            moved[name] = t
+    bt = inp.block_table.copy()
+    bt[bt >= 0] += base
+    moved["bt"] = torch.from_numpy(bt).cuda()
+    log("pages past 2 GiB (%s): cache %.2f GB, first used page at byte %d" % (
+        fmt, 2 * big["k"].numel() * big["k"].element_size() / 1e9, base * page_bytes))
+    _, lse_b, bits_b = run_decode(inp, dev=moved)
+    assert np.array_equal(bits_a, bits_b) and np.array_equal(lse_a, lse_b)
+    del big, moved, dev
+    torch.cuda.empty_cache()
+
+
 def medium_inputs(fmt="bf16", seed=5, **kw):
     c = cfg(num_q_heads=32, num_kv_heads=8, kv_format=fmt, page_size=64 if fmt == "fp8" else 16, **kw)
     sl = [1, 64, 300, 1023, 2500, 4096]
