@@ -58,3 +58,33 @@ def rel_l2(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def pages_past_two_gib(inp, dev):
+    """Device copies with the cache's pages moved to physical indices whose byte offsets
+    lie past 2^31: a cache of base + n pages whose first `base` pages are NaN (e4m3fn
+    0x7F for fp8; scales NaN), pages base .. base+n-1 the original ones, and the block
+    table shifted by base. Returns (moved dev dict, base, cache bytes per tensor)."""
+    import torch
+    fp8 = inp.kv_format != "bf16"
+    page_bytes = inp.num_kv_heads * inp.page_size * inp.head_dim * (1 if fp8 else 2)
+    base = (1 << 31) // page_bytes + 7
+    n = dev["k"].shape[0]
+    moved = dict(dev)
+    for name in ("k", "v"):
+        t = torch.empty((base + n,) + tuple(dev[name].shape[1:]), dtype=dev[name].dtype, device="cuda")
+        if fp8:
+            t.fill_(0x7F)
+        else:
+            t.fill_(float("nan"))
+        t[base:] = dev[name]
+        moved[name] = t
+    if fp8:
+        for name in ("ks", "vs"):
+            t = torch.full((base + n,) + tuple(dev[name].shape[1:]), float("nan"), device="cuda")
+            t[base:] = dev[name]
+            moved[name] = t
+    bt = inp.block_table.copy()
+    bt[bt >= 0] += base
+    moved["bt"] = torch.from_numpy(bt).cuda()
+    return moved, base, moved["k"].numel() * moved["k"].element_size()

@@ -9,7 +9,7 @@ import pytest
 
 import synth
 from oracle import append as OA
-from tests.gpu_util import device_inputs, log, run_decode
+from tests.gpu_util import device_inputs, log, pages_past_two_gib, run_decode
 from tests.test_gpu_parity import check
 
 pytestmark = pytest.mark.gpu
@@ -170,3 +170,34 @@ def test_decode_after_append_matches_oracle(fmt):
     dev["q"] = torch.from_numpy(q_rot.view(np.int16)).view(torch.bfloat16).cuda()
     out, lse, _ = run_decode(inp, dev=dev)
     check(inp, out, lse, tag="append + decode " + fmt)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_pages_past_two_gib(fmt):
+    """Appending into pages moved past 2^31 bytes of a ~2.2 GB cache tensor writes the
+    same bits (codes and scales) as appending into the compact cache, and nothing
+    before the moved pages."""
+    import torch
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2)
+    inp = synth.make_inputs(c, seed=35, slack_pages=2, seq_lens=[2, 17, 64, 65, 300, 1000])
+    k_new, v_new, q = synth.new_token_rows(inp, seed=36)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    dev = device_inputs(inp)
+    moved, base, _ = pages_past_two_gib(inp, dev)
+    head = moved["k"][:base].view(torch.int16 if fmt == "bf16" else torch.uint8)[-4:].clone()
+    q1 = gpu_append(inp, dev, k_new, v_new, q, rope)
+    q2 = gpu_append(inp, moved, k_new, v_new, q, rope)
+    assert np.array_equal(q1, q2)
+    small = cache_bits(dev, inp)
+    big = {name: moved[name][base:] for name in ("k", "v", "ks", "vs") if moved.get(name) is not None}
+    for name, x in zip(("k", "v", "ks", "vs"), small):
+        if x is None:
+            continue
+        y = big[name]
+        y = y.view(torch.int16).cpu().numpy().view(np.uint16) if y.dtype == torch.bfloat16 else y.cpu().numpy()
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), name
+    after = moved["k"][:base].view(torch.int16 if fmt == "bf16" else torch.uint8)[-4:]
+    assert torch.equal(head, after)
+    log("  append pages past 2 GiB (%s): first used page %d" % (fmt, base))
+    del moved, dev
+    torch.cuda.empty_cache()

@@ -18,7 +18,8 @@ import pytest
 import oracle
 import synth
 from oracle.formats import E4M3FN_TABLE, bf16_bits_to_f64
-from tests.gpu_util import device_inputs, log, make_runner, max_abs, rel_l2, run_decode
+from tests.gpu_util import (device_inputs, log, make_runner, max_abs, pages_past_two_gib, rel_l2,
+                            run_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -156,38 +157,18 @@ def test_million_token_request(fmt):
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_pages_past_two_gib(fmt):
     """The same pages moved to physical indices whose byte offsets lie past 2^31 in a
-    2.4 GB cache (the rest of it NaN, never read): bit-identical to the compact cache."""
+    ~2.2 GB cache tensor (the rest of it NaN, never read): bit-identical to the compact
+    cache."""
     import torch
     c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2)
     inp = synth.make_inputs(c, seed=43, seq_lens=[2, 300, 1000, 5000])
     dev = device_inputs(inp)
     _, lse_a, bits_a = run_decode(inp, dev=dev)
-    page_bytes = inp.num_kv_heads * inp.page_size * inp.head_dim * (1 if fmt == "fp8" else 2)
-    base = (1 << 31) // page_bytes + 7                 # first page past 2 GiB, plus some
-    n = inp.k_cache.shape[0]
-    big = {}
-    for name in ("k", "v"):
-        t = torch.full((base + n,) + tuple(dev[name].shape[1:]), float("nan") if fmt == "bf16" else 0,
-                       dtype=dev[name].dtype, device="cuda")
-        if fmt == "fp8":
-            t.fill_(0x7F)                              # e4m3fn NaN
-        t[base:] = dev[name]
-        big[name] = t
-    moved = dict(dev)
-    moved["k"], moved["v"] = big["k"], big["v"]
-    if fmt == "fp8":
-        for name in ("ks", "vs"):
-            t = torch.full((base + n,) + tuple(dev[name].shape[1:]), float("nan"), device="cuda")
-            t[base:] = dev[name]
-            moved[name] = t
-    bt = inp.block_table.copy()
-    bt[bt >= 0] += base
-    moved["bt"] = torch.from_numpy(bt).cuda()
-    log("pages past 2 GiB (%s): cache %.2f GB, first used page at byte %d" % (
-        fmt, 2 * big["k"].numel() * big["k"].element_size() / 1e9, base * page_bytes))
+    moved, base, nbytes = pages_past_two_gib(inp, dev)
+    log("pages past 2 GiB (%s): %.2f GB per cache tensor, first used page %d" % (fmt, nbytes / 1e9, base))
     _, lse_b, bits_b = run_decode(inp, dev=moved)
     assert np.array_equal(bits_a, bits_b) and np.array_equal(lse_a, lse_b)
-    del big, moved, dev
+    del moved, dev
     torch.cuda.empty_cache()
 
 

@@ -15,7 +15,7 @@ import pytest
 
 import synth
 from oracle.prefill import prefill_attention
-from tests.gpu_util import device_inputs, log, max_abs, rel_l2
+from tests.gpu_util import device_inputs, log, max_abs, pages_past_two_gib, rel_l2
 from tests.test_gpu_parity import LSE_TOL, REL_TOL, TOL, excess
 
 pytestmark = pytest.mark.gpu
@@ -195,3 +195,20 @@ def test_negative_and_zero_scale(scale):
     out, lse, _ = run_prefill(p)
     ref_out, ref_lse = prefill_attention(p)
     compare(p, out, lse, ref_out, ref_lse, "scale_%g" % scale)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_pages_past_two_gib(fmt):
+    """The prompts' pages moved past 2^31 bytes into a ~2.2 GB cache tensor (the rest
+    NaN): bit-identical output and lse."""
+    import torch
+    p = synth.make_prefill_inputs(cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16), seed=24,
+                                  q_lens=[70, 130], prefix=[30, 200])
+    dev = device_prefill(p)
+    o1, l1, a = run_prefill(p, dev=dev)
+    moved, base, nbytes = pages_past_two_gib(p.cache, dev)
+    log("  prefill pages past 2 GiB (%s): first used page %d" % (fmt, base))
+    o2, l2, b = run_prefill(p, dev=moved)
+    assert np.array_equal(a, b) and np.array_equal(l1, l2)
+    del moved, dev
+    torch.cuda.empty_cache()
