@@ -189,6 +189,39 @@ def _ptr(t, name="argument"):
                     % (name, type(t).__name__ if not hasattr(t, "device") else "a tensor on %s" % t.device))
 
 
+def _check_tensor(t, name, dtypes, shape, device):
+    """Argument check of the runners, which pass raw device addresses to kernels that
+    assume a layout: ``t`` must be a contiguous CUDA tensor on ``device``, of one of
+    ``dtypes``, with ``shape`` (None = any extent). Raises TypeError or ValueError."""
+    if not (hasattr(t, "data_ptr") and getattr(t, "is_cuda", False)):
+        raise TypeError("%s must be a CUDA tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, the runner on %s" % (name, t.device, device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s; expected %s" % (name, t.dtype, " or ".join(map(str, dtypes))))
+    if len(t.shape) != len(shape) or any(e is not None and int(a) != e for a, e in zip(t.shape, shape)):
+        raise ValueError("%s has shape %s; expected [%s]" % (
+            name, tuple(t.shape), ", ".join("*" if e is None else str(e) for e in shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_cache(k_cache, v_cache, k_scale, v_scale, num_kv_heads, page_size, head_dim, kv_format,
+                 device):
+    """K/V caches [num_pages, Hkv, P, D] (bf16, or e4m3fn bytes as uint8 or float8_e4m3fn)
+    and, for fp8, fp32 scales [num_pages, Hkv]. Returns num_pages."""
+    import torch
+    fp8 = kv_format in ("fp8", KV_FP8_E4M3FN)
+    kinds = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
+    _check_tensor(k_cache, "k_cache", kinds, (None, num_kv_heads, page_size, head_dim), device)
+    n = int(k_cache.shape[0])
+    _check_tensor(v_cache, "v_cache", kinds, (n, num_kv_heads, page_size, head_dim), device)
+    if fp8:
+        for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _check_tensor(t, name, (torch.float32,), (n, num_kv_heads), device)
+    return n
+
+
 def _stream_handle(stream):
     if stream is None:
         import torch
@@ -435,8 +468,26 @@ class PagedPrefill:
         """q bf16 [total, Hq, D]; cu_q / kv_lens device int32; q_lens_h / kv_lens_h host
         copies (for the plan). ``items``: a device plan from ``plan`` to reuse."""
         torch = self.torch
+        Hq, D, dev = self.num_q_heads, self.head_dim, self.device
+        _check_tensor(cu_q, "cu_q", (torch.int32,), (None,), dev)
+        B = int(cu_q.shape[0]) - 1
+        if B < 0:
+            raise ValueError("cu_q needs batch + 1 entries")
+        _check_tensor(q, "q", (torch.bfloat16,), (None, Hq, D), dev)
+        _check_tensor(kv_lens, "kv_lens", (torch.int32,), (B,), dev)
+        _check_tensor(block_table, "block_table", (torch.int32,), (B, None), dev)
+        _check_cache(k_cache, v_cache, k_scale, v_scale, self.num_kv_heads, self.page_size, D,
+                     self.kv_format, dev)
+        if len(q_lens_h) != B or len(kv_lens_h) != B:
+            raise ValueError("q_lens_h and kv_lens_h need one entry per request")
+        if out is not None:
+            _check_tensor(out, "out", (torch.bfloat16,), tuple(q.shape), dev)
+        if lse is not None:
+            _check_tensor(lse, "lse", (torch.float32,), (int(q.shape[0]), Hq), dev)
         if items is None:
             items = self.plan(q_lens_h, kv_lens_h)
+        else:
+            _check_tensor(items, "items", (torch.int32,), (None, 4), dev)
         if out is None:
             out = torch.empty_like(q)
         pkv_prefill(q=q, cu_q=cu_q, kv_lens=kv_lens, block_table=block_table, items=items,
@@ -631,6 +682,22 @@ class PagedDecode:
         """Enqueue the fused KV append for this runner's shapes: the step's new k/v rows
         (bf16 [B, Tq, Hkv, D]) into the paged cache, optionally rotating q into q_out and
         the k rows by the tables (fp32 [max_pos, D/2]); fp8 pages are quantised on write."""
+        torch, dev = self.torch, self.device
+        Tq, Hq, Hkv, D = self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim
+        _check_tensor(seq_lens, "seq_lens", (torch.int32,), (None,), dev)
+        B = int(seq_lens.shape[0])
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            _check_tensor(t, name, (torch.bfloat16,), (B, Tq, Hkv, D), dev)
+        _check_tensor(block_table, "block_table", (torch.int32,), (B, None), dev)
+        _check_cache(k_cache, v_cache, k_scale, v_scale, Hkv, self.page_size, D, self.kv_format, dev)
+        if (q is None) != (q_out is None) or (rope_cos is None) != (rope_sin is None):
+            raise ValueError("q and q_out, and rope_cos and rope_sin, come in pairs")
+        for t, name in ((q, "q"), (q_out, "q_out")):
+            if t is not None:
+                _check_tensor(t, name, (torch.bfloat16,), (B, Tq, Hq, D), dev)
+        for t, name in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+            if t is not None:
+                _check_tensor(t, name, (torch.float32,), (int(rope_cos.shape[0]), D // 2), dev)
         pkv_kv_append(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
                       block_table=block_table, seq_lens=seq_lens, num_pages=k_cache.shape[0],
                       batch=int(seq_lens.shape[0]), q_len=self.q_len, num_q_heads=self.num_q_heads,
@@ -664,7 +731,23 @@ class PagedDecode:
                             block_mask_h=block_mask_h)
         torch = self.torch
         Hkv, G = self.num_kv_heads, self.num_q_heads // self.num_kv_heads
+        Tq, Hq, D, dev = self.q_len, self.num_q_heads, self.head_dim, self.device
+        if seq_lens is not None:
+            _check_tensor(seq_lens, "seq_lens", (torch.int32,), (None,), dev)
         B = int(seq_lens.shape[0]) if seq_lens is not None else len(seq_lens_h)
+        if seq_lens_h is not None and len(seq_lens_h) != B:
+            raise ValueError("seq_lens_h has %d entries, seq_lens %d" % (len(seq_lens_h), B))
+        _check_tensor(q, "q", (torch.bfloat16,), (B, Tq, Hq, D), dev)
+        _check_tensor(block_table, "block_table", (torch.int32,), (B, None), dev)
+        _check_cache(k_cache, v_cache, k_scale, v_scale, Hkv, self.page_size, D, self.kv_format, dev)
+        if out is not None:
+            _check_tensor(out, "out", (torch.bfloat16,), (B, Tq, Hq, D), dev)
+        if lse_out is not None:
+            _check_tensor(lse_out, "lse_out", (torch.float32,), (B, Tq, Hq), dev)
+        if block_mask is not None:
+            _check_tensor(block_mask, "block_mask", (torch.uint8,), (B, Hkv, None), dev)
+            if block_mask_h is not None and tuple(np.shape(block_mask_h)) != tuple(block_mask.shape):
+                raise ValueError("block_mask_h must have block_mask's shape")
         bt_stride = block_table.shape[1]
         if block_mask is not None:
             # The one-kv-head problem: B * Hkv requests over the cache viewed as
