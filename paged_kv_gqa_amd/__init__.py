@@ -112,11 +112,11 @@ def _load():
         "pkv_abi_version": (ctypes.c_int, []),
         "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pkv_last_error": (ctypes.c_char_p, []),
-        "pkv_plan_query": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        "pkv_plan_query": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, _i32p, _i64p, _i64p]),
-        "pkv_plan": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_int, _i32p, _i32p, _i32p]),
+        "pkv_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
         "pkv_default_num_workers": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    ctypes.POINTER(ctypes.c_int)]),
         "pkv_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -593,6 +593,9 @@ class PagedDecode:
         self.max_items = max_items
         self._dev = None
         self._sparse = None
+        self._fmt = KV_FORMATS.get(kv_format, kv_format)
+        T, N, NP = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+        self._query_out = (T, N, NP, ctypes.byref(T), ctypes.byref(N), ctypes.byref(NP))
 
     def close(self):
         """Free the plan buffers (after the kernels that read them have completed)."""
@@ -612,36 +615,48 @@ class PagedDecode:
 
     def plan(self, seq_lens_h, num_q_heads=None, num_kv_heads=None):
         """Host plan into the next plan buffer; returns a dict describing it. The head
-        counts default to the runner's (block-sparse steps plan a one-kv-head problem)."""
+        counts default to the runner's (block-sparse steps plan a one-kv-head problem).
+        The buffer holds seq_lens [B], then items [N][4], worker offsets [W+1] and the
+        tile prefix [B+1], each 16-byte aligned; the planner reads and writes it by
+        address (numpy's ctypes conversions would cost several microseconds each)."""
         Hq = num_q_heads or self.num_q_heads
         Hkv = num_kv_heads or self.num_kv_heads
         sl = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
-        T, N, NP = pkv_plan_query(sl, self.q_len, Hq, Hkv, self.head_dim, self.page_size,
-                                  self.kv_format, self.tile_tokens, self.num_workers)
         W, B = self.num_workers, len(sl)
-        n_off = 4 * N
-        n_rtb = n_off + _round4(W + 1)
-        n_sl = n_rtb + _round4(B + 1)
-        total = n_sl + _round4(B)
+        n_items = _round4(B)
         k = self._slot
         self._slot = (k + 1) % len(self._bufs)
         if self._consumed[k] is not None:
             self._consumed[k].synchronize()        # the kernels that last read this buffer are done
         buf = self._bufs[k]
-        if buf is None or buf.nbytes < 4 * total:
-            if buf is not None:
-                buf.free()
-            buf = HostPlanBuffer(4 * max(total, 1024))
-            self._bufs[k] = buf
-        h = buf.array
-        pkv_plan(sl, self.q_len, Hkv, T, W,
-                 out=(h[:n_off].reshape(N, 4), h[n_off:n_off + W + 1], h[n_rtb:n_rtb + B + 1]))
-        h[n_sl:n_sl + B] = sl
+        if buf is None or buf.nbytes < 4 * (n_items + 4096):
+            buf = self._grow(k, 4 * (n_items + 4096))
+        buf.array[:B] = sl
         a = buf.addr
-        p = dict(T=T, N=N, NP=NP, W=W, B=B, slot=k, items=a, worker_offsets=a + 4 * n_off,
-                 req_tile_base=a + 4 * n_rtb, seq_lens=a + 4 * n_sl)
+        q = self._query_out
+        _check(_lib.pkv_plan_query(B, a, self.q_len, Hq, Hkv, self.head_dim, self.page_size,
+                                   self._fmt, self.tile_tokens, W, q[3], q[4], q[5]), "pkv_plan_query")
+        T, N, NP = q[0].value, q[1].value, q[2].value
+        n_off = n_items + 4 * N
+        n_rtb = n_off + _round4(W + 1)
+        total = n_rtb + _round4(B + 1)
+        if buf.nbytes < 4 * total:
+            buf = self._grow(k, 4 * total)
+            buf.array[:B] = sl
+            a = buf.addr
+        _check(_lib.pkv_plan(B, a, self.q_len, Hkv, T, W, a + 4 * n_items, a + 4 * n_off,
+                             a + 4 * n_rtb), "pkv_plan")
+        p = dict(T=T, N=N, NP=NP, W=W, B=B, slot=k, items=a + 4 * n_items,
+                 worker_offsets=a + 4 * n_off, req_tile_base=a + 4 * n_rtb, seq_lens=a)
         self.last_plan = p
         return p
+
+    def _grow(self, k, nbytes):
+        """Replace plan buffer k (idle: its kernels have completed) by one of nbytes."""
+        if self._bufs[k] is not None:
+            self._bufs[k].free()
+        self._bufs[k] = HostPlanBuffer(nbytes)
+        return self._bufs[k]
 
     def default_capacity(self, batch, bt_stride, num_kv_heads=None):
         """Item capacity of a device-built plan. For a fixed tile: the most items any
@@ -760,6 +775,7 @@ class PagedDecode:
             if block_mask_h is not None and tuple(np.shape(block_mask_h)) != tuple(block_mask.shape):
                 raise ValueError("block_mask_h must have block_mask's shape")
         bt_stride = block_table.shape[1]
+        sh = torch.cuda.current_stream(dev).cuda_stream   # one lookup for every launch below
         if block_mask is not None:
             # The one-kv-head problem: B * Hkv requests over the cache viewed as
             # [num_pages * Hkv, 1, P, D].
@@ -771,7 +787,7 @@ class PagedDecode:
                                      batch=B, num_kv_heads=Hkv, q_len=self.q_len,
                                      page_size=self.page_size, bt_stride=bt_stride,
                                      mask_stride=mask_stride, num_pages=k_cache.shape[0],
-                                     bt_out=sp["bt"], seq_lens_out=sp["sl"])
+                                     bt_out=sp["bt"], seq_lens_out=sp["sl"], stream=sh)
             prob = dict(batch=B * Hkv, Hq=G, Hkv=1, split=Hkv, bt=sp["bt"], sl=sp["sl"],
                         num_pages=k_cache.shape[0] * Hkv)
             use_device_plan = self.device_plan or block_mask_h is None
@@ -794,7 +810,7 @@ class PagedDecode:
                             tile_tokens=self.tile_tokens, num_workers=self.num_workers,
                             max_items=d["cap"], items=d["items"], worker_offsets=d["offsets"],
                             req_tile_base=d["rtb"], info=d["info"], scratch=d["scratch"],
-                            scratch_bytes=d["scratch_bytes"])
+                            scratch_bytes=d["scratch_bytes"], stream=sh)
             p = dict(T=self.tile_tokens, N=d["cap"], NP=d["cap"], W=self.num_workers, slot=None,
                      items=d["items"], worker_offsets=d["offsets"], req_tile_base=d["rtb"])
             tile_dev = d["info"][1:]
@@ -817,13 +833,13 @@ class PagedDecode:
                            page_size=self.page_size, bt_stride=bt_stride,
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
                            scale=scale, k_scale=k_scale, v_scale=v_scale, tile_tokens_dev=tile_dev,
-                           request_split=prob["split"])
+                           request_split=prob["split"], stream=sh)
         if partial_events is not None:
             partial_events[1].record()
         pkv_combine_split(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
                           req_tile_base=p["req_tile_base"], batch=prob["batch"], q_len=self.q_len,
                           num_q_heads=prob["Hq"], num_kv_heads=prob["Hkv"], head_dim=self.head_dim,
-                          request_split=prob["split"], out=out, lse_out=lse_out)
+                          request_split=prob["split"], out=out, lse_out=lse_out, stream=sh)
         k = p["slot"]
         if k is not None:
             if self._consumed[k] is None:
