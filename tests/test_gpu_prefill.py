@@ -212,3 +212,21 @@ def test_pages_past_two_gib(fmt):
     assert np.array_equal(a, b) and np.array_equal(l1, l2)
     del moved, dev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_chunk_after_million_token_prefix(fmt):
+    """A 2048-token chunk after a 1 000 000-token prefix, beside a short prompt: query
+    positions past 2^20, each tile walking ~31 300 key blocks through ~62 600 block-table
+    entries (bf16 pages of 16); sampled rows of both requests against the oracle."""
+    import torch
+    p = synth.make_prefill_inputs(cfg(num_q_heads=4, num_kv_heads=1, kv_format=fmt,
+                                      page_size=64 if fmt == "fp8" else 16),
+                                  seed=25, q_lens=[2048, 50], prefix=[1_000_000, 3])
+    log("  chunk after a 1M-token prefix (%s): %d pages" % (fmt, p.cache.k_cache.shape[0]))
+    out, lse, _ = run_prefill(p)
+    rows = sample_rows(p, np.random.default_rng(3), per_request=6)
+    ref_out, ref_lse = prefill_attention(p, pairs=[(0, 0), (1, 0)], rows=rows)
+    compare(p, out, lse, ref_out, ref_lse, "1M prefix %s" % fmt)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    torch.cuda.empty_cache()
