@@ -201,3 +201,24 @@ def test_pages_past_two_gib(fmt):
     log("  append pages past 2 GiB (%s): first used page %d" % (fmt, base))
     del moved, dev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_append_at_million_token_positions(fmt):
+    """Four new tokens per request at positions past 10^6, both crossing a page boundary
+    (999 999 | 1 000 000 and 1 048 575 | 1 048 576), rotated by tables of ~1.05M
+    positions: the whole cache, the scales and the rotated q bit for bit."""
+    import torch
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=4, num_q_heads=4,
+            num_kv_heads=1)
+    inp = synth.make_inputs(c, seed=36, seq_lens=[1_000_003, 1_048_578])
+    k_new, v_new, q = synth.new_token_rows(inp, seed=37)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    dev = device_inputs(inp)
+    log("append at 1M positions (%s): %d pages, tables of %d positions" % (
+        fmt, inp.k_cache.shape[0], rope[0].shape[0]))
+    q_gpu = gpu_append(inp, dev, k_new, v_new, q, rope)
+    q_ref = oracle_append(inp, k_new, v_new, q, rope)
+    assert_same(inp, dev, q_gpu, q_ref, "1M positions " + fmt)
+    del dev
+    torch.cuda.empty_cache()
