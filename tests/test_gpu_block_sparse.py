@@ -157,3 +157,24 @@ def test_full_size_sparse_sampled(name, keep):
     check_sparse(inp, mask, out, lse, pairs=sample_pairs(inp), tag="%s keep %.2f" % (name, keep))
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_million_token_request(fmt):
+    """A 1 000 003-token request with about 40 % of its pages attended, beside a short
+    one, two kv heads (masks differ per head), two draft tokens: the compaction walks
+    ~62 500 mask bytes per row (bf16 pages of 16); host and device plans give the same
+    bits, every row checked against the oracle."""
+    import torch
+    c = cfg(q_len=2, num_q_heads=4, num_kv_heads=2, kv_format=fmt, page_size=64 if fmt == "fp8" else 16)
+    inp = synth.make_inputs(c, seed=44, seq_lens=[1_000_003, 300])
+    mask = synth.make_block_mask(inp, 0.4, seed=45)
+    dev = device_inputs(inp)
+    log("block-sparse 1M-token request (%s): %d pages, %d mask bytes per row" % (
+        fmt, inp.k_cache.shape[0], mask.shape[-1]))
+    out, lse, bits = run_sparse(inp, mask, dev=dev)
+    check_sparse(inp, mask, out, lse, tag="sparse 1M %s" % fmt)
+    _, lse_d, bits_d = run_sparse(inp, mask, device_plan=True, dev=dev)
+    assert np.array_equal(bits, bits_d) and np.array_equal(lse, lse_d)
+    del dev
+    torch.cuda.empty_cache()
