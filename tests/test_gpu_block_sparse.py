@@ -178,3 +178,55 @@ def test_million_token_request(fmt):
     assert np.array_equal(bits, bits_d) and np.array_equal(lse, lse_d)
     del dev
     torch.cuda.empty_cache()
+
+
+def test_graph_replay_with_new_masks_and_lengths():
+    """Compaction + device plan + decode + combine captured once, replayed with new
+    device masks and lengths; every replay equals an eager host-planned block-sparse
+    step bit for bit."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    c = cfg(q_len=2, num_q_heads=16, num_kv_heads=4)
+    B = 16
+    inp = synth.make_inputs(dict(c, batch=B), seed=46, seq_lens=np.full(B, 5000, np.int32))
+    dev = device_inputs(inp)
+    rng = np.random.default_rng(47)
+    r = pkv.PagedDecode(num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16, q_len=2,
+                        device_plan=True)
+    static_sl = dev["sl"].clone()
+    static_mask = torch.from_numpy(synth.make_block_mask(inp, 0.5, seed=48)).cuda()
+    out = torch.empty((B, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 2, 16), dtype=torch.float32, device="cuda")
+
+    def step():
+        r(dev["q"], dev["k"], dev["v"], dev["bt"], None, inp.scale, seq_lens=static_sl, out=out,
+          lse_out=lse, block_mask=static_mask)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                      # buffers and workspace exist before the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    host = pkv.PagedDecode(num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16, q_len=2)
+    for rep in range(4):
+        new_sl = np.maximum(rng.integers(2, 5001, B), 2).astype(np.int32)
+        new_mask = synth.make_block_mask(inp, [0.1, 0.5, 0.9, 0.3][rep], seed=49 + rep)
+        static_sl.copy_(torch.from_numpy(new_sl))
+        static_mask.copy_(torch.from_numpy(new_mask))
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_lse = out.view(torch.int16).cpu().numpy().copy(), lse.cpu().numpy().copy()
+        ref_lse = torch.empty_like(lse)
+        ref = host(dev["q"], dev["k"], dev["v"], dev["bt"], new_sl, inp.scale,
+                   seq_lens=torch.from_numpy(new_sl).cuda(), lse_out=ref_lse,
+                   block_mask=torch.from_numpy(new_mask).cuda(), block_mask_h=new_mask)
+        torch.cuda.synchronize()
+        info = r.plan_info()
+        log("  replay %d: %s" % (rep, info))
+        assert info["status"] == 0
+        assert np.array_equal(got, ref.view(torch.int16).cpu().numpy()), rep
+        assert np.array_equal(got_lse, ref_lse.cpu().numpy()), rep
