@@ -222,3 +222,77 @@ def test_append_at_million_token_positions(fmt):
     assert_same(inp, dev, q_gpu, q_ref, "1M positions " + fmt)
     del dev
     torch.cuda.empty_cache()
+
+
+def test_graph_captured_step_with_append():
+    """A whole decode step with no host work - fused append (rotation, paged write) of
+    the step's token, device plan, decode, combine - captured once in a HIP graph and
+    replayed for four successive tokens with new rows and lengths; every replay's
+    output, and the cache at the end, bit for bit those of the same steps run eagerly
+    with host plans on a second copy of the cache."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    c = cfg(num_q_heads=16, num_kv_heads=4)
+    lens = np.array([1, 15, 16, 17, 300, 1000, 2047], np.int32)
+    inp = synth.make_inputs(c, seed=50, slack_pages=8, seq_lens=lens + 5)   # room for 5 tokens
+    inp.seq_lens[:] = lens
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    cos, sin = (torch.from_numpy(x).cuda() for x in rope)
+    dev_g, dev_e = device_inputs(inp), device_inputs(inp)
+    kw = dict(num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16)
+    r_g, r_e = pkv.PagedDecode(device_plan=True, **kw), pkv.PagedDecode(**kw)
+    as_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    B = inp.batch
+    kn, vn = (torch.empty((B, 1, 4, 128), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    qn = torch.empty((B, 1, 16, 128), dtype=torch.bfloat16, device="cuda")
+    q_rot = torch.empty_like(qn)
+    sl = dev_g["sl"]
+    out = torch.empty((B, 1, 16, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1, 16), dtype=torch.float32, device="cuda")
+
+    def next_token(step):
+        inp.seq_lens += 1
+        k_h, v_h, q_h = synth.new_token_rows(inp, seed=60 + step)
+        kn.copy_(as_bf16(k_h)); vn.copy_(as_bf16(v_h)); qn.copy_(as_bf16(q_h))
+        sl.copy_(torch.from_numpy(inp.seq_lens))
+
+    def graph_step():
+        r_g.append(kn, vn, dev_g["k"], dev_g["v"], dev_g["bt"], sl, q=qn, q_out=q_rot,
+                   rope_cos=cos, rope_sin=sin)
+        r_g(q_rot, dev_g["k"], dev_g["v"], dev_g["bt"], None, inp.scale, seq_lens=sl, out=out,
+            lse_out=lse)
+
+    def eager_step():
+        sl_e = torch.from_numpy(inp.seq_lens.copy()).cuda()
+        q_e = torch.empty_like(qn)
+        r_e.append(kn.clone(), vn.clone(), dev_e["k"], dev_e["v"], dev_e["bt"], sl_e, q=qn.clone(),
+                   q_out=q_e, rope_cos=cos, rope_sin=sin)
+        lse_e = torch.empty_like(lse)
+        o = r_e(q_e, dev_e["k"], dev_e["v"], dev_e["bt"], inp.seq_lens.copy(), inp.scale,
+                seq_lens=sl_e, lse_out=lse_e)
+        return o, lse_e
+
+    next_token(0)                   # first token: eager on both copies (allocates buffers)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        graph_step()
+    torch.cuda.current_stream().wait_stream(s)
+    eager_step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graph_step()
+    for step in range(1, 5):
+        next_token(step)
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_lse = out.view(torch.int16).cpu().numpy().copy(), lse.cpu().numpy().copy()
+        ref, ref_lse = eager_step()
+        torch.cuda.synchronize()
+        assert r_g.plan_info()["status"] == 0
+        assert np.array_equal(got, ref.view(torch.int16).cpu().numpy()), step
+        assert np.array_equal(got_lse, ref_lse.cpu().numpy()), step
+        log("  token %d: replay equals the eager step" % step)
+    for name in ("k", "v"):
+        assert torch.equal(dev_g[name].view(torch.int16), dev_e[name].view(torch.int16)), name
