@@ -358,6 +358,9 @@ def main():
                     help="start every step with the fused KV append (rotary embedding of q "
                          "and the new k rows, paged write, fp8 quantise-on-write) of the "
                          "batch's newest tokens")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --device-plan: time the step replayed from a HIP graph captured once "
+                         "(the kernel is timed on eager steps)")
     ap.add_argument("--device-plan", action="store_true",
                     help="build the plan on the GPU (pkv_plan_device) from device seq_lens "
                          "instead of on the host")
@@ -376,6 +379,10 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.graph and (not args.device_plan or args.block_sparse is not None):
+        print("--graph needs --device-plan (a host plan cannot be replayed) and no --block-sparse",
+              file=sys.stderr)
         sys.exit(2)
     if args.prefill is not None:
         prefill_main(args)
@@ -465,6 +472,20 @@ def main():
     K = args.steps
     log("timing %d steps" % K)
     wall, kern_avg_s, n_timed = timed_steps(step, K, args.event_every)
+    if args.graph:
+        # The same step captured once; the graph's replays are the timed steps.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_desc += ", replayed from a HIP graph"
     ms_per_step = wall / K * 1e3
     value = algo / (wall / K) / 1e9
     achieved = partial_algo / kern_avg_s / 1e9
@@ -521,7 +542,8 @@ def main():
     }
     if not args.no_distribution:
         log("step distribution: back to back and flushed, %d steps each" % args.dist_steps)
-        dist = step_distribution(lambda: step(), dev, n=args.dist_steps)
+        dist = step_distribution((lambda: g.replay()) if args.graph else (lambda: step()), dev,
+                                 n=args.dist_steps)
         dist["host_plan_us"] = None if args.device_plan else host_plan_us(
             inp, args.tile_tokens, plan["W"])
         dist["plan_upload_us"] = 0.0 if not args.device_plan else None
