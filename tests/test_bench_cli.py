@@ -22,6 +22,13 @@ def test_more_than_one_gpu_exits_with_a_message():
 def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
-    for flag in ("--workload", "--prefill", "--device-plan", "--block-sparse", "--append",
+    for flag in ("--workload", "--prefill", "--device-plan", "--graph", "--block-sparse", "--append",
                  "--event-every", "--ramp-ms", "--no-read-probe"):
         assert flag in r.stdout, flag
+
+
+def test_graph_needs_a_device_plan():
+    for args in (("--graph",), ("--graph", "--device-plan", "--block-sparse", "0.5")):
+        r = run(*args)
+        assert r.returncode == 2 and "--graph needs --device-plan" in r.stderr, args
+        assert r.stdout == ""
