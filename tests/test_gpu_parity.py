@@ -94,6 +94,8 @@ SMALL = [
     dict(id="g4_d128_p48", c=cfg(page_size=48), sl=[1, 47, 48, 49, 95, 200, 1000], T=96, W=5),
     dict(id="spec2_g8_d64_p48_auto", c=cfg(page_size=48, num_q_heads=16, head_dim=64, q_len=2),
          sl=[2, 48, 97, 2000, 4801], T=0, W=9),
+    dict(id="fp8_d64_spec4_g4", c=cfg(kv_format="fp8", page_size=64, head_dim=64, q_len=4),
+         sl=[4, 5, 63, 64, 65, 67, 130, 1000, 4097], T=128, W=6),
 ]
 
 
