@@ -92,6 +92,10 @@ SMALL = [
     dict(id="g8_p64_keep25", c=cfg(num_q_heads=16, page_size=64), keep=0.25, T=128, W=9),
     dict(id="fp8_spec2_keep50", c=cfg(kv_format="fp8", page_size=64, q_len=2), keep=0.5, T=0, W=0),
     dict(id="fp8_spec4_g4_keep30", c=cfg(kv_format="fp8", page_size=64, q_len=4), keep=0.3, T=64, W=11),
+    dict(id="p48_d64_spec2_keep40", c=cfg(page_size=48, head_dim=64, q_len=2, num_q_heads=16),
+         keep=0.4, T=96, W=5),
+    dict(id="fp8_d64_spec4_keep60", c=cfg(kv_format="fp8", page_size=64, head_dim=64, q_len=4),
+         keep=0.6, T=0, W=0),
 ]
 LENS = [1, 16, 17, 63, 64, 65, 200, 777, 1500, 3000]
 
