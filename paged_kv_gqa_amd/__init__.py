@@ -519,6 +519,18 @@ _HIP_HOST_MALLOC_MAPPED = 0x2
 _HIP_HOST_MALLOC_COHERENT = 0x40000000
 
 
+def _hip_runtime():
+    """The HIP runtime torch has loaded (dlopen by soname returns the loaded copy): the
+    ROCm 7 soname first, then older and unversioned ones."""
+    err = None
+    for name in ("libamdhip64.so.7", "libamdhip64.so.6", "libamdhip64.so"):
+        try:
+            return ctypes.CDLL(name)
+        except OSError as e:
+            err = e
+    raise ImportError("no HIP runtime (libamdhip64) could be loaded: %s" % err)
+
+
 class HostPlanBuffer:
     """Pinned, device-mapped, coherent host memory for one step's plan.
 
@@ -530,7 +542,7 @@ class HostPlanBuffer:
 
     def __init__(self, nbytes):
         if HostPlanBuffer._hip is None:
-            hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
+            hip = _hip_runtime()
             hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
             hip.hipHostMalloc.restype = ctypes.c_int
             hip.hipHostFree.argtypes = [ctypes.c_void_p]
