@@ -8,9 +8,9 @@
 namespace pkv {
 
 // Waves per decode workgroup (one workgroup = one planner worker).
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
 // Decode workgroups resident per compute unit that the default worker count assumes.
-constexpr int kDecodeGroupsPerCU = 2;
+constexpr int kDecodeGroupsPerCU = 1;
 // Largest M = G * Tq one work item may carry (one MFMA column block).
 constexpr int kMaxRows = 16;
 
