@@ -7,7 +7,8 @@
 // be merged by the combine kernel.
 //
 // Mapping onto CDNA4 (wave64, MFMA 16x16x32 bf16):
-// - The four waves of a workgroup split a tile into 32-token chunks, round-robin.
+// - The waves of a workgroup (kDecodeWaves, eight: one workgroup per CU) split a tile
+//   into 32-token chunks, round-robin.
 //   A chunk is two 16-token halves; each half lies inside one page because pages
 //   and tiles are multiples of 16 tokens.
 // - Operands are swapped so the KV tokens fill the MFMA's 16-row side and the
