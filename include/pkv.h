@@ -177,7 +177,11 @@ typedef struct pkv_decode_args {
 } pkv_decode_args;
 
 /*
- * Split-KV partial attention: one persistent workgroup per worker walks its
+ * Split-KV partial attention (HALOps README, "Highlights": paged-KV decode attention
+ * with GQA, BF16/FP8 KV, speculative decoding and split-KV; HPC-Ops review, "How the
+ * kernels are organized around specific workload shapes": each uniform tile assigned
+ * before the step yields a partial result that a separate kernel merges). One
+ * persistent workgroup per worker walks its
  * items; for item (b, g, i) it gathers the tile's K/V pages through the block
  * table, runs an online softmax over the tile and writes, for each of the M rows
  * r = t*G + j (query token t, head g*G + j), the normalised partial output o
@@ -237,7 +241,10 @@ int pkv_plan_device(const int32_t* seq_lens, int batch, int q_len, int num_q_hea
                     void* scratch, size_t scratch_bytes, void* stream);
 
 /*
- * Log-sum-exp merge of the partials of each row (b, t, h):
+ * Combine (HPC-Ops review, "How the kernels are organized around specific workload
+ * shapes": a kernel of its own merges the split-KV partial results; HALOps README,
+ * "Highlights": the reduction adapts to each request, so a request cut into one tile
+ * is only normalised and cast). Log-sum-exp merge of the partials of each row (b, t, h):
  *   M* = max_i lse_i, w_i = exp(lse_i - M*), out = sum_i w_i o_i / sum_i w_i,
  *   lse_out = M* + ln sum_i w_i,   i = 0 .. n_b - 1 in order (deterministic),
  * n_b = req_tile_base[b+1] - req_tile_base[b] (device array). out is written in

@@ -42,13 +42,3 @@ def e4m3fn_to_f64(codes):
     """uint8 e4m3fn codes -> float64 (exact)."""
     return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
 
-
-def f64_to_bf16_f64(x):
-    """Round float64 values to the nearest bf16 value (ties to even), returned as
-    float64. Used only to describe how the HIP path rounds its output."""
-    x = np.asarray(x, dtype=np.float64)
-    f = x.astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u >> np.uint64(16)) & np.uint64(1)
-    u = ((u + np.uint64(0x7FFF) + r) >> np.uint64(16)) << np.uint64(16)
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)

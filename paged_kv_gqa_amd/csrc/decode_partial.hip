@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   const int first = worker_offsets[blockIdx.x];
   const int last = worker_offsets[blockIdx.x + 1];
 
-  // The wave's work is a stream of units (item, chunk): chunks wid, wid + 4, ... of
+  // The wave's work is a stream of units (item, chunk): chunks wid, wid + kWaves, ... of
   // each of the worker's items. `raw` always holds the next unit's K/V in flight, and
   // `qf_next` the query fragment of its item, so an item's first chunk is loaded
   // while the previous item is still being computed and merged.

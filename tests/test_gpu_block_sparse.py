@@ -1,14 +1,14 @@
 """Block-sparse decode on an MI355X against the fp64 oracle: the device compaction
 bit for bit, whole steps (host and device plan, bf16 and fp8 KV, draft tokens) to the
 decode tolerances, masked pages never read, and the full mixed and fp8 workloads
-under a sampled oracle check."""
+with every (request, kv head) group against the oracle."""
 
 import numpy as np
 import pytest
 
 import synth
 from tests.gpu_util import device_inputs, log
-from tests.test_gpu_parity import check, sample_pairs
+from tests.test_gpu_parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -151,14 +151,15 @@ def test_masked_pages_are_never_read(fmt):
 
 
 @pytest.mark.parametrize("name,keep", [("mixed", 0.25), ("fp8_spec", 0.5)])
-def test_full_size_sparse_sampled(name, keep):
+def test_full_size_sparse(name, keep):
     import torch
     log("full-size sparse %s keep %.2f: generating inputs" % (name, keep))
     inp = synth.make_inputs(synth.ALL[name], seed=0)
     mask = synth.make_block_mask(inp, keep, seed=1)
     out, lse, _ = run_sparse(inp, mask)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
-    check_sparse(inp, mask, out, lse, pairs=sample_pairs(inp), tag="%s keep %.2f" % (name, keep))
+    log("full-size sparse %s: oracle over all %d groups" % (name, inp.batch * inp.num_kv_heads))
+    check_sparse(inp, mask, out, lse, tag="%s keep %.2f" % (name, keep))
     del inp
     torch.cuda.empty_cache()
 

@@ -55,6 +55,16 @@ def excess(out, ref, tol):
     return float(np.max(err - np.maximum(tol, 0.6 * bf16_ulp(ref)), initial=-np.inf))
 
 
+def ulp_branch(out, ref, tol):
+    """Elements whose bound is the 0.6-ulp one (it exceeds the flat tolerance) and
+    the largest error among them, as (count, max_abs)."""
+    ref = np.asarray(ref, np.float64)
+    sel = 0.6 * bf16_ulp(ref) > tol
+    if not sel.any():
+        return 0, 0.0
+    return int(sel.sum()), float(np.max(np.abs(np.asarray(out, np.float64)[sel] - ref[sel])))
+
+
 def check(inp, out, lse, pairs=None, tag="", block_mask=None):
     ref_out, ref_lse = oracle.decode_attention(inp, pairs=pairs, block_mask=block_mask)
     if pairs is not None:
@@ -65,9 +75,12 @@ def check(inp, out, lse, pairs=None, tag="", block_mask=None):
         out, ref_out = out[sel], ref_out[sel]
         lse, ref_lse = lse[sel], ref_lse[sel]
     assert np.isfinite(out).all() and np.isfinite(lse).all(), tag
+    tol = TOL[inp.kv_format]
     ea, er, el = max_abs(out, ref_out), rel_l2(out, ref_out), max_abs(lse, ref_lse)
-    log("  %s: max_abs %.3e rel_l2 %.3e lse %.3e" % (tag, ea, er, el))
-    assert excess(out, ref_out, TOL[inp.kv_format]) <= 0, tag
+    nu, eu = ulp_branch(out, ref_out, tol)
+    log("  %s: %d outputs, max_abs %.3e rel_l2 %.3e lse %.3e; ulp branch %d outputs, max_abs %.3e"
+        % (tag, np.size(out), ea, er, el, nu, eu))
+    assert excess(out, ref_out, tol) <= 0, tag
     assert er <= REL_TOL, tag
     assert el <= LSE_TOL, tag
 
@@ -110,25 +123,17 @@ def test_small_cases_match_oracle(case):
     check(inp, out, lse, tag=case["id"])
 
 
-def sample_pairs(inp, n=10, seed=0):
-    rng = np.random.default_rng(seed)
-    sl = inp.seq_lens
-    picks = {int(np.argmax(sl)), int(np.argmin(sl))}
-    picks |= set(int(b) for b in rng.choice(inp.batch, size=min(n, inp.batch), replace=False))
-    return sorted({(b, int(rng.integers(inp.num_kv_heads))) for b in picks} | {(int(np.argmax(sl)), 0)})
-
-
 @pytest.mark.parametrize("name", ["llama8b", "mixed", "long", "fp8_spec"])
-def test_full_size_workloads_sampled(name):
+def test_full_size_workloads(name):
     """The full workloads in the launch configuration the bench times (automatic tile
-    size, default worker count); the oracle checks sampled (request, kv head) groups."""
+    size, default worker count); every (request, kv head) group against the oracle."""
     import torch
     log("full-size %s: generating inputs" % name)
     inp = synth.make_inputs(synth.ALL[name], seed=0)
     log("full-size %s: running" % name)
     out, lse, _ = run_decode(inp)
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    check(inp, out, lse, pairs=sample_pairs(inp), tag=name)
+    log("full-size %s: oracle over all %d groups" % (name, inp.batch * inp.num_kv_heads))
+    check(inp, out, lse, tag=name)
     del inp
     torch.cuda.empty_cache()
 

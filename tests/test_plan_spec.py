@@ -126,16 +126,3 @@ def test_auto_tile_hand_worked():
     # fp8 with page 16: the quantum is lcm(16, 64) = 64
     assert P.tile_quantum(16, "fp8") == 64 and P.tile_quantum(64, "fp8") == 64
     assert P.tile_quantum(32, "bf16") == 32
-
-
-@pytest.mark.parametrize("name,T,N", [("tiny", 16, 29), ("llama8b", 65536, 512), ("mixed", 16384, 1224),
-                                      ("long", 4096, 256), ("fp8_spec", 8192, 424)])
-def test_auto_tile_on_workloads(name, T, N):
-    import synth
-    cfg = synth.ALL[name]
-    sl = synth.draw_seq_lens(cfg, np.random.default_rng(0))
-    t = P.auto_tile_tokens(sl, cfg["q_len"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"],
-                           cfg["page_size"], cfg["kv_format"], 512)
-    assert t == T
-    p = P.lpt_plan(sl, cfg["num_kv_heads"], t, 512)
-    assert len(p["items"]) == N
