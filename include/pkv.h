@@ -71,7 +71,7 @@ enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum, ... */
   PKV_ERR_UNSUPPORTED = -2,  /* D not 64/128; P not a multiple of 16; fp8 with P != 64;
-                                Hq % Hkv != 0; Tq not in [1, 4]; M > 16; tile not a
+                                Hq % Hkv != 0; Tq not in [1, 4]; M > 64; tile not a
                                 multiple of the quantum */
   PKV_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
   PKV_ERR_WORKSPACE = -4,    /* workspace smaller than pkv_workspace_bytes() */

@@ -38,7 +38,7 @@ PKV_ERR_WORKSPACE = -4
 PKV_ERR_HIP = -5
 PKV_ERR_SEQ = -6
 
-MAX_ROWS = 16  # largest (q heads per kv head) x (query tokens) per work item
+MAX_ROWS = 64  # largest (q heads per kv head) x (query tokens) per work item
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)

@@ -7,30 +7,40 @@
 // be merged by the combine kernel.
 //
 // Mapping onto CDNA4 (wave64, MFMA 16x16x32 bf16):
-// - The waves of a workgroup (kDecodeWaves, eight: one workgroup per CU) split a tile
-//   into 32-token chunks, round-robin.
-//   A chunk is two 16-token halves; each half lies inside one page because pages
-//   and tiles are multiples of 16 tokens.
+// - The waves of a workgroup split a tile into 32-token chunks, round-robin. A chunk
+//   is two 16-token halves; each half lies inside one page because pages and tiles
+//   are multiples of 16 tokens.
 // - Operands are swapped so the KV tokens fill the MFMA's 16-row side and the
 //   M = G*Tq query rows of the kv head sit on the 16-column side (the "swap A/B"
 //   idea of the HPC-Ops launch article, section on aligning task traits with the
-//   hardware, re-derived for MFMA). Lane l owns query row n = l % 16 for the whole
-//   softmax, so row max, row sum and rescale factors never leave the lane except
-//   for one exchange across the four 16-lane groups.
+//   hardware, re-derived for MFMA). M <= 16 is one column block; up to 64 rows (wide
+//   GQA groups with draft tokens) take NB = 2 or 4 blocks that share every K/V
+//   operand. Lane l owns query row 16*nb + l % 16 of block nb for the whole softmax,
+//   so row max, row sum and rescale factors never leave the lane except for one
+//   exchange across the four 16-lane groups.
 // - K and V stream from HBM with non-temporal 16-byte loads, each wave instruction
 //   reading 1 KB of whole 128-byte lines of a 16-token half: on MI355X only
 //   full-line non-temporal reads reach ~6.8 TB/s on a random 4 KB page gather
 //   (half-line or cached reads stop near 6.1 TB/s). Each wave stages its chunk in
-//   its own LDS region (XOR-swizzled 16-byte units, so the reads below hit distinct
-//   banks) and reads it back in the MFMA operand layout: lane l holds token l % 16 of
-//   a half, bytes 16*(l/16) + 64*u of its row. QK^T then needs no shuffling. P.V
-//   contracts over tokens, so V is transposed on the matrix core: an MFMA of the V
-//   half against a 0/1 selection matrix returns, in each lane, four consecutive
-//   tokens of one head dimension - the operand layout P.V needs - exactly (products
-//   by 1 and sums of zeros), in fp32, then packed back to bf16.
-// - FP8 (OCP e4m3fn) K/V bytes are widened to bf16 with the gfx950 conversion
-//   instruction (exact). The per-(page, kv head) scales are applied outside the
-//   products: the K scale multiplies the scores, the V scale multiplies P before P.V.
+//   its own LDS region:
+//   - K as stored (bf16 or e4m3fn), in XOR-swizzled 16-byte units, read back in the
+//     MFMA operand layout (lane l: token l % 16 of a half, bytes 16*(l/16) + 64*u of
+//     its row), so QK^T needs no shuffling;
+//   - V as 16-bit rows with a padded row stride, read back transposed by gfx950's
+//     ds_read_b64_tr_b16: P.V contracts over tokens, and the transposing read hands
+//     each lane four consecutive tokens of one head dimension, the operand layout V^T
+//     needs.
+// - FP8 (OCP e4m3fn) K bytes are widened to bf16 with the gfx950 conversion
+//   instruction (exact) and the page's K scale multiplies the scores. FP8 V bytes are
+//   converted on their way into LDS to fp16 (code x 2^e, exact: the conversion
+//   instruction applies a power-of-two scale), so P.V runs in fp16; the rest of the
+//   page's V scale, v_scale / 2^e in [1, 2), multiplies P.
+// - P enters the matrix cores as 16-bit numbers: fp16 for FP8 KV (2^-12 relative
+//   rounding), bf16 for bf16 KV (2^-9). With bf16, on a chunk where some row's
+//   largest weight may be a large share of that row's sum (a wave's first chunk of an
+//   item, rows that see few keys, a score far above the earlier ones), the low bf16
+//   part p - bf16(p) is multiplied into V as well, so the weights that dominate an
+//   output carry about 16 bits.
 // - The next chunk's loads are issued into the same registers as soon as the
 //   current chunk sits in LDS, so each wave keeps one chunk (16 KB for bf16) in
 //   flight while its matrix and vector work runs.
@@ -43,23 +53,42 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = kDecodeWaves;
-constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.69314718055994531f;
+// A chunk also multiplies the low bf16 part of P into V when, for some row, three
+// times the lane's largest new weight exceeds the lane's share of the row's sum so
+// far. That holds whenever a weight exceeds a quarter of the row's sum after the
+// chunk (the weight's own lane sees 4p > p + its earlier sum).
+constexpr float kLowPartTest = 3.f;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+// Two floats -> packed fp16 pair (round to nearest even; v_cvt_pk_f16_f32).
+__device__ __forceinline__ unsigned pack_f16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
 }
 
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
@@ -75,6 +104,24 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(unsigned w0, unsigned w1) {
   return r;
 }
 
+// Eight e4m3fn bytes -> eight fp16 values of code x scale, for a power-of-two scale
+// (exact while the result stays in fp16's normal and subnormal range).
+__device__ __forceinline__ u32x4 fp8x8_to_f16(unsigned w0, unsigned w1, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, scale, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, scale, true));
+  r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, scale, false));
+  r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, scale, true));
+  return r;
+}
+
+// Transposing LDS read of four 16-bit values: in each 16-lane group, lanes 4k..4k+3
+// address row k of a 4 x 16 tile and lane i receives column i (rows 0..3).
+__device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
 // Max over the four 16-lane groups (lanes n, n+16, n+32, n+48) with the gfx950
 // lane-swap instructions: each swap returns the value and its partner in every lane.
 __device__ __forceinline__ float group_max(float x) {
@@ -84,7 +131,12 @@ __device__ __forceinline__ float group_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D, bool FP8>
+__device__ __forceinline__ float max8(const float (&a)[8]) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+               fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+}
+
+template <int D, bool FP8, int NB>
 struct Cfg {
   static constexpr int kEb = FP8 ? 1 : 2;        // bytes per KV element
   static constexpr int kSteps = D / 32;           // MFMA k-steps over the head dimension
@@ -94,25 +146,38 @@ struct Cfg {
   static constexpr int kUnits = kRowBytes / 16;   // 16-byte units per token row
   // Rows per 256 bytes is a power of two; the swizzle uses rows / (256 / kRowBytes).
   static constexpr int kRowShift = kRowBytes == 256 ? 0 : (kRowBytes == 128 ? 1 : 2);
-  // Per-wave LDS: K and V stage (2 x 32 rows) or the wave's epilogue rows, whichever
-  // is larger, in 16-byte units.
-  static constexpr int kStageVec = 2 * 32 * kUnits > 4 * D ? 2 * 32 * kUnits : 4 * D;
+  // One column block: two waves per SIMD. Two or four blocks hold 2-4x the
+  // accumulators and query fragments: one wave per SIMD, with twice the registers.
+  static constexpr int kWaves = NB == 1 ? 8 : 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 16 * NB;
+  // bf16 KV: P.V in bf16, with P's low part on chunks that need it. FP8 KV: P.V in
+  // fp16 (V = code x scale converted on staging), precise enough without it.
+  static constexpr bool kLowPart = !FP8;
+  // Per-wave LDS (bytes): K rows [32] as stored, then V rows [32] as 16-bit with a
+  // stride of 2D + 32 bytes (the four rows of a transposing read fall in disjoint
+  // bank groups). After an item's last chunk the region holds the wave's
+  // unnormalised output rows, kMergeBlocks column blocks [16][D] fp32 at a time.
+  static constexpr int kKBytes = 32 * kRowBytes;
+  static constexpr int kVStride = 2 * D + 32;
+  static constexpr int kStageBytes = kKBytes + 32 * kVStride;
+  static constexpr int kMergeBlocks =
+      kStageBytes / (16 * D * 4) < NB ? kStageBytes / (16 * D * 4) : NB;
+  static constexpr int kMergeRounds = (NB + kMergeBlocks - 1) / kMergeBlocks;
+  // Four column blocks keep their query fragments in LDS (per wave, [NB][kSteps]
+  // 16-byte units in lane order) instead of 64 registers.
+  static constexpr bool kQInLds = NB > 2;
+  static constexpr int kQBytes = kQInLds ? NB * kSteps * 64 * 16 : 0;
+  static constexpr int kWaveBytes = kStageBytes + kQBytes;
+  static_assert(kMergeBlocks >= 1, "a column block's rows must fit a wave's region");
 };
 
-// Head-dimension index that k-step s, lane group gq, element e of an MFMA operand
-// holds. bf16: one 16-byte load per step. fp8: one 16-byte load serves two steps.
+// Head-dimension index that k-step s, lane group gq, element e of a QK^T operand
+// holds. bf16: one 16-byte K unit per step. fp8: one 16-byte unit serves two steps.
 template <bool FP8>
 __device__ __forceinline__ int op_dim(int s, int gq, int e) {
   if (FP8) return 64 * (s >> 1) + 16 * gq + 8 * (s & 1) + e;
   return 32 * s + 8 * gq + e;
-}
-
-// Head-dimension index of output value v in block (s, c) of lane group gq: the
-// selection matrix c picks operand column k = 16c + r, r = 4*gq + v.
-template <bool FP8>
-__device__ __forceinline__ int out_dim(int s, int c, int gq, int v) {
-  const int k = 16 * c + 4 * gq + v;
-  return op_dim<FP8>(s, k >> 3, k & 7);
 }
 
 struct ItemCtx {
@@ -148,21 +213,21 @@ __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chun
 }
 
 // One chunk as loaded: [K/V][half][instruction], 16 bytes per lane each.
-template <int D, bool FP8>
+template <int D, bool FP8, int NB>
 struct Raw {
-  u32x4 r[2][2][Cfg<D, FP8>::kLoads];
+  u32x4 r[2][2][Cfg<D, FP8, NB>::kLoads];
 };
 
 // Issue the chunk's loads: instruction j of half h reads bytes j*1024 + 16*lane of
 // the half's contiguous 16-row run (whole cache lines, non-temporal).
-template <int D, bool FP8>
-__device__ __forceinline__ void load_raw(Raw<D, FP8>& raw, const uint8_t* __restrict__ kc,
+template <int D, bool FP8, int NB>
+__device__ __forceinline__ void load_raw(Raw<D, FP8, NB>& raw, const uint8_t* __restrict__ kc,
                                          const uint8_t* __restrict__ vc, const HalfOffsets& ho,
                                          int lane) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < Cfg<D, FP8>::kLoads; ++j) {
+    for (int j = 0; j < Cfg<D, FP8, NB>::kLoads; ++j) {
       const int64_t off = ho.off[h] + j * 1024 + lane * 16;
       raw.r[0][h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + off));
       raw.r[1][h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + off));
@@ -170,134 +235,233 @@ __device__ __forceinline__ void load_raw(Raw<D, FP8>& raw, const uint8_t* __rest
   }
 }
 
-// Stage slot of 16-byte unit `unit` of chunk row `row` (0..31) of K (kv 0) or V (1).
-// The unit index is XOR-ed with the row's position among the rows that share a
-// 256-byte bank window, so 16 lanes reading one unit column of 16 rows hit 16
-// distinct 16-byte bank groups.
-template <int D, bool FP8>
-__device__ __forceinline__ int stage_slot(int kv, int row, int unit) {
-  using C = Cfg<D, FP8>;
-  return (kv * 32 + row) * C::kUnits + (unit ^ ((row >> C::kRowShift) & (C::kUnits - 1)));
+// K stage slot of 16-byte unit `unit` of chunk row `row` (0..31). The unit index is
+// XOR-ed with the row's position among the rows that share a 256-byte bank window,
+// so 16 lanes reading one unit column of 16 rows hit 16 distinct 16-byte bank groups.
+template <int D, bool FP8, int NB>
+__device__ __forceinline__ int k_slot(int row, int unit) {
+  using C = Cfg<D, FP8, NB>;
+  return row * C::kUnits + (unit ^ ((row >> C::kRowShift) & (C::kUnits - 1)));
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void stage_write(u32x4* __restrict__ st, const Raw<D, FP8>& raw, int lane) {
-  using C = Cfg<D, FP8>;
+// Stage a loaded chunk. V rows at or past `valid` (tokens past the tile end, which
+// may be unwritten cache memory) are stored as zeros, so that a zero probability
+// never meets a NaN in P.V. FP8 V codes are stored as fp16 code x v_pow2 (a power of
+// two).
+template <int D, bool FP8, int NB>
+__device__ __forceinline__ void stage_write(uint8_t* __restrict__ st, const Raw<D, FP8, NB>& raw,
+                                            int lane, int valid, float v_pow2) {
+  using C = Cfg<D, FP8, NB>;
+  u32x4* const kst = reinterpret_cast<u32x4*>(st);
+  uint8_t* const vst = st + C::kKBytes;
 #pragma unroll
-  for (int kv = 0; kv < 2; ++kv)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
-        const int pos = j * 1024 + lane * 16;
-        st[stage_slot<D, FP8>(kv, 16 * h + pos / C::kRowBytes, (pos % C::kRowBytes) / 16)] = raw.r[kv][h][j];
-      }
-}
-
-// Read the chunk back in MFMA operand layout: lane (n, gq) takes, for each half and
-// 16-byte piece u, bytes 64u + 16gq of token row n; fp8 pieces widen to two bf16
-// operand steps.
-template <int D, bool FP8>
-__device__ __forceinline__ void stage_read(const u32x4* __restrict__ st, u32x4 (&kop)[2][D / 32],
-                                           u32x4 (&vop)[2][D / 32], int n, int gq) {
-  using C = Cfg<D, FP8>;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int u = 0; u < C::kLoads; ++u) {
-      const u32x4 kr = st[stage_slot<D, FP8>(0, 16 * h + n, 4 * u + gq)];
-      const u32x4 vr = st[stage_slot<D, FP8>(1, 16 * h + n, 4 * u + gq)];
+    for (int j = 0; j < C::kLoads; ++j) {
+      const int pos = j * 1024 + lane * 16;
+      const int row = 16 * h + pos / C::kRowBytes;
+      const int unit = (pos % C::kRowBytes) / 16;
+      kst[k_slot<D, FP8, NB>(row, unit)] = raw.r[0][h][j];
+      u32x4 v = raw.r[1][h][j];
+      if (valid < 32 && row >= valid) v = u32x4{0u, 0u, 0u, 0u};
       if constexpr (FP8) {
-        kop[h][2 * u] = fp8x8_to_bf16(kr[0], kr[1]);
-        kop[h][2 * u + 1] = fp8x8_to_bf16(kr[2], kr[3]);
-        vop[h][2 * u] = fp8x8_to_bf16(vr[0], vr[1]);
-        vop[h][2 * u + 1] = fp8x8_to_bf16(vr[2], vr[3]);
+        u32x4* dst = reinterpret_cast<u32x4*>(vst + row * C::kVStride + 32 * unit);
+        dst[0] = fp8x8_to_f16(v[0], v[1], v_pow2);
+        dst[1] = fp8x8_to_f16(v[2], v[3], v_pow2);
       } else {
-        kop[h][u] = kr;
-        vop[h][u] = vr;
+        *reinterpret_cast<u32x4*>(vst + row * C::kVStride + 16 * unit) = v;
       }
+    }
+}
+
+// K operands of half h: lane (n, gq) takes bytes 64u + 16gq of token row 16h + n;
+// fp8 units widen to two bf16 operand steps.
+template <int D, bool FP8, int NB>
+__device__ __forceinline__ void read_k(const uint8_t* __restrict__ st, u32x4 (&kop)[D / 32], int h,
+                                       int n, int gq) {
+  using C = Cfg<D, FP8, NB>;
+  const u32x4* const kst = reinterpret_cast<const u32x4*>(st);
+#pragma unroll
+  for (int u = 0; u < C::kLoads; ++u) {
+    const u32x4 kr = kst[k_slot<D, FP8, NB>(16 * h + n, 4 * u + gq)];
+    if constexpr (FP8) {
+      kop[2 * u] = fp8x8_to_bf16(kr[0], kr[1]);
+      kop[2 * u + 1] = fp8x8_to_bf16(kr[2], kr[3]);
+    } else {
+      kop[u] = kr;
     }
   }
 }
 
-// Online-softmax update of one 32-token chunk. acc[blk] holds O^T for head-dim
-// block blk (lane: rows 4*gq+v of the block, column n); m in log2 units.
-template <int D, bool FP8>
-__device__ __forceinline__ void process_chunk(u32x4 (&kop)[2][D / 32], u32x4 (&vop)[2][D / 32],
-                                              const u32x4 (&qf)[D / 32],
-                                              const u32x4 (&sel)[2], f32x4 (&acc)[D / 16],
-                                              float& m, float& lsum, float& lexact, int j0, int lim,
-                                              int tile_end, float c_qk, float v_mul, int n,
+// Online-softmax state of the rows a lane owns (one per column block): running
+// maximum m (log2 units), the sum of the weights P.V used (the output's normaliser)
+// and the sum of the unrounded weights (the log-sum-exp's argument). Each lane
+// holds the sums of its own tokens; the row's four lanes are added at the end.
+template <int NB>
+struct RowState {
+  float m[NB], lsum[NB], lexact[NB];
+};
+
+// Online-softmax update of one 32-token chunk for every column block. acc[nb][bl]
+// holds O^T of head-dim block bl (lane: dims 16bl + 4gq + v, query row 16nb + n).
+// bf16 KV with one column block forms P's low parts only when the chunk needs them;
+// wider items form them with the high parts (fewer live registers: the unrounded
+// weights are not kept across the products) and read K once per block.
+template <int D, bool FP8, int NB, class QGet>
+__device__ __forceinline__ void process_chunk(const uint8_t* __restrict__ st, const QGet& qget,
+                                              f32x4 (&acc)[NB][D / 16], RowState<NB>& rs, int j0,
+                                              const int (&lim)[NB], float c_qk, float p_mul, int n,
                                               int gq) {
-  using C = Cfg<D, FP8>;
-  // Tokens at or past the tile end may be unwritten cache memory: zero their V so
-  // that a zero probability cannot meet a NaN in P.V. Lane l loaded token l % 16.
-  if (j0 + 32 > tile_end) {
+  using C = Cfg<D, FP8, NB>;
+  constexpr bool kLow = C::kLowPart;
+  constexpr bool kEagerLow = kLow && NB > 1;
+  float pv[kLow && !kEagerLow ? NB : 1][8];
+  u32x4 ph[NB], pl[kEagerLow ? NB : 1];
+  float psum[NB], plsum[kEagerLow ? NB : 1];
+  bool low = false;
+  // S^T = K . Q^T: lane (n, gq) gets tokens 16h + 4gq + v of query row 16nb + n.
+  f32x4 sacc1[NB == 1 ? 2 : 1];
+  if constexpr (NB == 1) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (j0 + 16 * h + n >= tile_end) {
+      u32x4 kop[C::kSteps];
+      read_k<D, FP8, NB>(st, kop, h, n, gq);
+      sacc1[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) vop[h][s] = u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < C::kSteps; ++s) sacc1[h] = mfma_bf16(kop[s], qget(0, s), sacc1[h]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    f32x4 sacc[2];
+    if constexpr (NB == 1) {
+      sacc[0] = sacc1[0];
+      sacc[1] = sacc1[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 kop[C::kSteps];
+        read_k<D, FP8, NB>(st, kop, h, n, gq);
+        sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) sacc[h] = mfma_bf16(kop[s], qget(nb, s), sacc[h]);
+      }
+    }
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + 16 * (e >> 2) + 4 * gq + (e & 3);
+      sv[e] = (j < lim[nb]) ? sacc[e >> 2][e & 3] * c_qk : -INFINITY;
+    }
+    const float lane_max = max8(sv);
+    const float m_new = fmaxf(rs.m[nb], group_max(lane_max));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(rs.m[nb] - m_use);
+    rs.lsum[nb] *= alpha;
+    rs.lexact[nb] *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int bl = 0; bl < C::kBlocks; ++bl) acc[nb][bl] *= alpha;
+    }
+    rs.m[nb] = m_new;
+    if constexpr (kLow) low |= kLowPartTest * __builtin_amdgcn_exp2f(lane_max - m_use) > rs.lexact[nb];
+    float p[8], pexact = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+      pexact += p[e];
+    }
+    rs.lexact[nb] += pexact;
+    if constexpr (FP8) {  // P.V weights carry the V scale's non-power-of-two part
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ph[nb][e] = pack_f16(p[2 * e] * p_mul, p[2 * e + 1] * p_mul);
+    } else {
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[nb][e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+        ps += bf16_lo(ph[nb][e]) + bf16_hi(ph[nb][e]);
+      }
+      psum[nb] = ps;
+    }
+    if constexpr (kEagerLow) {
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pl[nb][e] = pack_bf16(p[2 * e] - bf16_lo(ph[nb][e]), p[2 * e + 1] - bf16_hi(ph[nb][e]));
+        ls += bf16_lo(pl[nb][e]) + bf16_hi(pl[nb][e]);
+      }
+      plsum[nb] = ls;
+    } else if constexpr (kLow) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[nb][e] = p[e];
+    }
+  }
+
+  // V^T operands: dims 16bl + n, tokens 4gq + 0..3 then 16 + 4gq + 0..3 (lane (n, gq)
+  // addresses row 4gq + n / 4, dims 16bl + 4 (n % 4) of each four-row tile).
+  const uint8_t* const vbase = st + C::kKBytes + (4 * gq + (n >> 2)) * C::kVStride + 8 * (n & 3);
+  auto read_v = [&](int bl) {
+    const u32x2 lo = read_tr16(vbase + 32 * bl);
+    const u32x2 hi = read_tr16(vbase + 16 * C::kVStride + 32 * bl);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // O^T += V^T . P^T: the lane's eight weights (tokens 4gq + 0..3, 16 + 4gq + 0..3)
+  // are exactly the k-values of P^T's B operand.
+  auto pv_mfma = [&](u32x4 v, u32x4 w, f32x4 c) { return FP8 ? mfma_f16(v, w, c) : mfma_bf16(v, w, c); };
+  if constexpr (kEagerLow) {
+    // Wide items: one V operand at a time, high and (when needed) low parts
+    // accumulated on the matrix core (the accumulators live in AGPRs).
+    const bool low_chunk = __builtin_amdgcn_ballot_w64(low) != 0;
+#pragma unroll
+    for (int bl = 0; bl < C::kBlocks; ++bl) {
+      const u32x4 vop = read_v(bl);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb][bl] = mfma_bf16(vop, ph[nb], acc[nb][bl]);
+      if (low_chunk) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb][bl] = mfma_bf16(vop, pl[nb], acc[nb][bl]);
+      }
+    }
+    if (low_chunk) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) psum[nb] += plsum[nb];
+    }
+  } else {
+    u32x4 vop[C::kBlocks];
+#pragma unroll
+    for (int bl = 0; bl < C::kBlocks; ++bl) vop[bl] = read_v(bl);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int bl = 0; bl < C::kBlocks; ++bl) acc[nb][bl] = pv_mfma(vop[bl], ph[nb], acc[nb][bl]);
+    if constexpr (kLow) {
+      if (__builtin_amdgcn_ballot_w64(low)) {
+        // The low part goes through a fresh accumulator and is added in place, so the
+        // accumulators keep their registers whichever way this branch goes.
+        __asm__ volatile("");
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          u32x4 pln;
+          float ls = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pln[e] = pack_bf16(pv[nb][2 * e] - bf16_lo(ph[nb][e]), pv[nb][2 * e + 1] - bf16_hi(ph[nb][e]));
+            ls += bf16_lo(pln[e]) + bf16_hi(pln[e]);
+          }
+          psum[nb] += ls;
+#pragma unroll
+          for (int bl = 0; bl < C::kBlocks; ++bl)
+            acc[nb][bl] += mfma_bf16(vop[bl], pln, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
       }
     }
   }
-
-  // S^T = K . Q^T: lane (n, gq) gets tokens 16h + 4gq + v of query row n.
-  f32x4 st[2];
+  // bf16 KV: the normaliser is the sum of the weights P.V used, so V = 1 gives
+  // exactly 1. FP8 KV: the unrounded sum (fp16 weights are within 2^-12 of it).
+  if constexpr (!FP8) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    st[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) st[h] = mfma_bf16(kop[h][s], qf[s], st[h]);
-  }
-  float sv[8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = j0 + 16 * h + 4 * gq + v;
-      sv[4 * h + v] = (j < lim) ? st[h][v] * c_qk : -INFINITY;
-    }
-  }
-  float cm = sv[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
-  cm = group_max(cm);
-  const float m_new = fmaxf(m, cm);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-  unsigned pk[4];
-  float psum = 0.f, pexact = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float p0 = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
-    const float p1 = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
-    const unsigned u = pack_bf16(p0, p1);
-    psum += bf16_lo(u) + bf16_hi(u);   // normaliser: the rounded weights P.V sees
-    pexact += p0 + p1;                 // log-sum-exp: the unrounded weights
-    pk[e] = FP8 ? pack_bf16(p0 * v_mul, p1 * v_mul) : u;
-  }
-  lsum = lsum * alpha + psum;
-  lexact = lexact * alpha + pexact;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-    for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
-  }
-  m = m_new;
-  const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
-
-  // V^T via the selection MFMA, then O^T += V^T . P^T.
-#pragma unroll
-  for (int s = 0; s < C::kSteps; ++s) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 x0 = mfma_bf16(vop[0][s], sel[c], zero);
-      const f32x4 x1 = mfma_bf16(vop[1][s], sel[c], zero);
-      const u32x4 va = {pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]),
-                        pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
-      acc[2 * s + c] = mfma_bf16(va, pb, acc[2 * s + c]);
-    }
+    for (int nb = 0; nb < NB; ++nb) rs.lsum[nb] += psum[nb];
   }
 }
 
@@ -314,12 +478,12 @@ struct ItemInfo {
   int b, g, slot, L, nchunks;
 };
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NB>
 __device__ __forceinline__ ItemInfo item_info(const int32_t* __restrict__ items,
                                               const int32_t* __restrict__ seq_lens,
                                               const int32_t* __restrict__ block_table,
                                               const DecodeShape& sh, int itx) {
-  using C = Cfg<D, FP8>;
+  using C = Cfg<D, FP8, NB>;
   ItemInfo r;
   r.b = items[4 * itx + 0];
   r.g = items[4 * itx + 1];
@@ -337,42 +501,32 @@ __device__ __forceinline__ ItemInfo item_info(const int32_t* __restrict__ items,
   return r;
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_kernel(
+template <int D, bool FP8, int NB>
+__global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_cache,
     const uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
     const int32_t* __restrict__ worker_offsets, const int32_t* __restrict__ tile_dev,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, const DecodeShape sh_arg) {
-  using C = Cfg<D, FP8>;
+  using C = Cfg<D, FP8, NB>;
+  constexpr int kWaves = C::kWaves;
+  constexpr int kThreads = C::kThreads;
   // The tile size comes from the launch, or from device memory when a device-built
   // plan chose it.
   DecodeShape sh = sh_arg;
   if (tile_dev != nullptr) sh.tile_tokens = __builtin_amdgcn_readfirstlane(tile_dev[0]);
-  // Each wave's region stages its chunks and, after its last chunk of an item,
-  // holds its unnormalised output rows [16][D] for the merge.
-  __shared__ u32x4 lds_stage[kWaves][C::kStageVec];
-  __shared__ float lds_m[kWaves][kMaxRows];
-  __shared__ float lds_l[kWaves][kMaxRows];
-  __shared__ float lds_le[kWaves][kMaxRows];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_stage[kWaves][C::kWaveBytes];
+  __shared__ float lds_m[kWaves][C::kRows];
+  __shared__ float lds_l[kWaves][C::kRows];
+  __shared__ float lds_le[kWaves][C::kRows];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int n = lane & 15;   // query row owned by this lane (and K/V row it reads)
   const int gq = lane >> 4;  // 16-lane group
-  u32x4* const my_stage = lds_stage[wid];
-
-  // Selection matrices: sel[c] has a 1 where operand k = 16c + n (bf16 1.0 = 0x3f80).
-  u32x4 sel[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int e = 16 * c + n - 8 * gq;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      sel[c][w] = (e == 2 * w ? 0x3f80u : 0u) | (e == 2 * w + 1 ? 0x3f800000u : 0u);
-  }
+  uint8_t* const my_stage = lds_stage[wid];
 
   const int M = sh.rows;
   const int Tq = sh.q_len;
@@ -380,12 +534,15 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   const int first = worker_offsets[blockIdx.x];
   const int last = worker_offsets[blockIdx.x + 1];
 
-  // The wave's work is a stream of units (item, chunk): chunks wid, wid + kWaves, ... of
-  // each of the worker's items. `raw` always holds the next unit's K/V in flight, and
-  // `qf_next` the query fragment of its item, so an item's first chunk is loaded
-  // while the previous item is still being computed and merged.
-  Raw<D, FP8> raw;
-  u32x4 qf_next[C::kSteps];
+  // The wave's work is a stream of units (item, chunk): chunks wid, wid + kWaves, ...
+  // of each of the worker's items. `raw` always holds the next unit's K/V in flight,
+  // so an item's first chunk is loaded while the previous item is still being
+  // computed and merged. With one column block `qf_next` prefetches the query
+  // fragments of that item as well; wider items load theirs when the item starts
+  // (their registers go to the extra accumulators).
+  constexpr bool kPrefetchQ = NB == 1;
+  Raw<D, FP8, NB> raw;
+  u32x4 qf_next[kPrefetchQ ? NB : 1][C::kSteps];
   // FP8: the K and V page scales of the unit in flight, loaded with its K/V so that
   // their dependent loads (block-table entry, then scale) stay off the compute path.
   float ksc_next = 1.f, vsc_next = 1.f;
@@ -394,7 +551,7 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
   auto find_unit = [&](int from) {  // first unit of this wave in items >= from
     u_itx = -1;
     for (int x = from; x < last; ++x) {
-      const ItemInfo inf = item_info<D, FP8>(items, seq_lens, block_table, sh, x);
+      const ItemInfo inf = item_info<D, FP8, NB>(items, seq_lens, block_table, sh, x);
       if (wid < inf.nchunks) {
         u_itx = x;
         u_c = wid;
@@ -403,32 +560,40 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
       }
     }
   };
+  // Query fragments of kv head g of work-list request b: row r = 16nb + n is draft
+  // token r / G of query head g*G + r % G (rows r >= M are zero).
+  auto load_q = [&](u32x4 (&dst)[NB][C::kSteps], int b, int g) {
+    // q is [B / split, Tq, split * Hq, D]; with split 1 this is [B, Tq, Hq, D].
+    const int split = sh.request_split;
+    const int64_t qb = (split == 1) ? b : b / split;
+    const int part = (split == 1) ? 0 : b - static_cast<int>(qb) * split;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = 16 * nb + n;
+      if (r < M) {
+        const int t = r / G;
+        const int head = g * G + (r - t * G);
+        const uint16_t* qrow = q + (((qb * Tq + t) * split + part) * sh.num_q_heads + head) * D;
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s)
+          dst[nb][s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
+      } else {
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) dst[nb][s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
   auto issue_unit = [&]() {
     if (u_itx < 0) return;
     const HalfOffsets ho = chunk_offsets(u_info.it, u_c);
-    load_raw<D, FP8>(raw, k_cache, v_cache, ho, lane);
+    load_raw<D, FP8, NB>(raw, k_cache, v_cache, ho, lane);
     if constexpr (FP8) {
       const int64_t sidx = ho.phys0 * sh.num_kv_heads + u_info.g;
       ksc_next = k_scale[sidx];
       vsc_next = v_scale[sidx];
     }
-    if (u_c == wid) {  // first chunk of an item: fetch that item's query fragment
-      if (n < M) {
-        const int t = n / G;
-        const int head = u_info.g * G + (n - t * G);
-        // q is [B / split, Tq, split * Hq, D]; with split 1 this is [B, Tq, Hq, D].
-        const int split = sh.request_split;
-        const int64_t qb = (split == 1) ? u_info.b : u_info.b / split;
-        const int part = (split == 1) ? 0 : u_info.b - static_cast<int>(qb) * split;
-        const uint16_t* qrow =
-            q + (((qb * Tq + t) * split + part) * sh.num_q_heads + head) * D;
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s)
-          qf_next[s] = *reinterpret_cast<const u32x4*>(qrow + op_dim<FP8>(s, gq, 0));
-      } else {
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) qf_next[s] = u32x4{0u, 0u, 0u, 0u};
-      }
+    if constexpr (kPrefetchQ) {
+      if (u_c == wid) load_q(qf_next, u_info.b, u_info.g);  // first chunk of an item
     }
   };
   find_unit(first);
@@ -436,119 +601,184 @@ __global__ __launch_bounds__(kThreads, kDecodeGroupsPerCU) void decode_partial_k
 
   for (int itx = first; itx < last; ++itx) {
     const ItemInfo cur = (u_itx == itx) ? u_info
-                                        : item_info<D, FP8>(items, seq_lens, block_table, sh, itx);
-    // Causal limit of row n (draft token t sees keys up to L - Tq + t); padding rows
-    // n >= M see the whole tile.
-    int lim = cur.it.tile_end;
-    if (n < M) lim = min(lim, cur.L - Tq + n / G + 1);
-    u32x4 qf[C::kSteps];
+                                        : item_info<D, FP8, NB>(items, seq_lens, block_table, sh, itx);
+    // Causal limit of each row (draft token t sees keys up to L - Tq + t); padding
+    // rows r >= M see the whole tile.
+    int lim[NB];
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) qf[s] = qf_next[s];
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = 16 * nb + n;
+      lim[nb] = cur.it.tile_end;
+      if (r < M) lim[nb] = min(lim[nb], cur.L - Tq + r / G + 1);
+    }
+    u32x4 qf[C::kQInLds ? 1 : NB][C::kSteps];
+    u32x4* const qlds = reinterpret_cast<u32x4*>(my_stage + C::kStageBytes);
+    if constexpr (kPrefetchQ) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) qf[nb][s] = qf_next[nb][s];
+    } else if (u_itx == itx) {
+      if constexpr (C::kQInLds) {
+        u32x4 qt[NB][C::kSteps];
+        load_q(qt, cur.b, cur.g);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int s = 0; s < C::kSteps; ++s) qlds[(nb * C::kSteps + s) * 64 + lane] = qt[nb][s];
+      } else {
+        load_q(qf, cur.b, cur.g);
+      }
+    }
+    auto qget = [&](int nb, int s) -> u32x4 {
+      if constexpr (C::kQInLds)
+        return qlds[(nb * C::kSteps + s) * 64 + lane];
+      else
+        return qf[nb][s];
+    };
 
-    f32x4 acc[C::kBlocks];
+    f32x4 acc[NB][C::kBlocks];
+    RowState<NB> rs;
 #pragma unroll
-    for (int bl = 0; bl < C::kBlocks; ++bl) acc[bl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.f, lexact = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int bl = 0; bl < C::kBlocks; ++bl) acc[nb][bl] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rs.m[nb] = -INFINITY;
+      rs.lsum[nb] = 0.f;
+      rs.lexact[nb] = 0.f;
+    }
 
     while (u_itx == itx) {
       const int c = u_c;
-      stage_write<D, FP8>(my_stage, raw, lane);
-      float c_qk = sh.qk_scale_log2, v_mul = 1.f;
-      if constexpr (FP8) {  // this unit's scales, before issue_unit loads the next's
-        c_qk = sh.qk_scale_log2 * ksc_next;
-        v_mul = vsc_next;
+      const int j0 = cur.it.tile_start + 32 * c;
+      // This unit's page scales are used before issue_unit loads the next unit's. The V
+      // scale splits into v_pow2 = 2^e, applied exactly when V is converted to fp16,
+      // and p_mul = v_scale / 2^e, in [1, 2) while e lies in [-15, 7].
+      float c_qk = sh.qk_scale_log2, p_mul = 1.f, v_pow2 = 1.f;
+      if constexpr (FP8) {
+        c_qk *= ksc_next;
+        int e;
+        (void)frexpf(vsc_next, &e);
+        const int e1 = min(max(e - 1, -15), 7);
+        v_pow2 = ldexpf(1.f, e1);
+        p_mul = ldexpf(vsc_next, -e1);
       }
+      stage_write<D, FP8, NB>(my_stage, raw, lane, cur.it.tile_end - j0, v_pow2);
       if (c + kWaves < cur.nchunks)
         u_c = c + kWaves;
       else
         find_unit(itx + 1);
       issue_unit();
-      u32x4 kop[2][C::kSteps], vop[2][C::kSteps];
-      stage_read<D, FP8>(my_stage, kop, vop, n, gq);
-      process_chunk<D, FP8>(kop, vop, qf, sel, acc, m, lsum, lexact, cur.it.tile_start + 32 * c, lim,
-                            cur.it.tile_end, c_qk, v_mul, n, gq);
+      process_chunk<D, FP8, NB>(my_stage, qget, acc, rs, j0, lim, c_qk, p_mul, n, gq);
     }
 
-    // Wave result -> LDS: row max, full row sums, unnormalised O.
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    lexact += __shfl_xor(lexact, 16);
-    lexact += __shfl_xor(lexact, 32);
-    if (gq == 0) {
-      lds_m[wid][n] = m;
-      lds_l[wid][n] = lsum;
-      lds_le[wid][n] = lexact;
+    // Wave result -> LDS: row max and full row sums, then the unnormalised rows of
+    // kMergeBlocks column blocks per round, merged across the waves.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float ls = FP8 ? rs.lexact[nb] : rs.lsum[nb];
+      float le = rs.lexact[nb];
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      le += __shfl_xor(le, 16);
+      le += __shfl_xor(le, 32);
+      if (gq == 0) {
+        lds_m[wid][16 * nb + n] = rs.m[nb];
+        lds_l[wid][16 * nb + n] = ls;
+        lds_le[wid][16 * nb + n] = le;
+      }
     }
-    float* const my_rows = reinterpret_cast<float*>(my_stage);   // [16][D]
+    float* const my_rows = reinterpret_cast<float*>(my_stage);
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s)
+    for (int round = 0; round < C::kMergeRounds; ++round) {
+      if (round > 0) __syncthreads();  // the previous round's rows have been merged
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int k = 0; k < C::kMergeBlocks; ++k) {
+        const int nb = round * C::kMergeBlocks + k;
+        if (nb < NB) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) my_rows[n * D + out_dim<FP8>(s, c, gq, v)] = acc[2 * s + c][v];
-    __syncthreads();
+          for (int bl = 0; bl < C::kBlocks; ++bl)
+            *reinterpret_cast<f32x4*>(my_rows + (16 * k + n) * D + 16 * bl + 4 * gq) = acc[nb][bl];
+        }
+      }
+      __syncthreads();
 
-    // Merge the waves' partial softmax states and write the item's partial.
-    float* wo = ws_o + static_cast<int64_t>(cur.slot) * M * D;
-    for (int e = tid; e < M * D; e += kThreads) {
-      const int r = e / D, d = e - r * D;
+      // Merge the waves' partial softmax states of this round's rows and write them.
+      const int r0 = 16 * C::kMergeBlocks * round;
+      const int r1 = min(M, r0 + 16 * C::kMergeBlocks);
+      float* wo = ws_o + static_cast<int64_t>(cur.slot) * M * D;
+      for (int e = r0 * D + tid; e < r1 * D; e += kThreads) {
+        const int r = e / D, d = e - r * D;
+        float mx = lds_m[0][r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w][r]);
+        float o = 0.f;
+        if (mx != -INFINITY) {
+          float num = 0.f, den = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float f = __builtin_amdgcn_exp2f(lds_m[w][r] - mx);
+            num += f * reinterpret_cast<const float*>(lds_stage[w])[(r - r0) * D + d];
+            den += f * lds_l[w][r];
+          }
+          o = num / den;
+        }
+        wo[e] = o;
+      }
+    }
+    for (int r = tid; r < M; r += kThreads) {
       float mx = lds_m[0][r];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w][r]);
-      float o = 0.f;
-      if (mx != -INFINITY) {
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float f = __builtin_amdgcn_exp2f(lds_m[w][r] - mx);
-          num += f * reinterpret_cast<const float*>(lds_stage[w])[r * D + d];
-          den += f * lds_l[w][r];
-        }
-        o = num / den;
-      }
-      wo[e] = o;
-    }
-    if (tid < M) {
-      float mx = lds_m[0][tid];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w][tid]);
       float lse = -INFINITY;
       if (mx != -INFINITY) {
         float den = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][tid] - mx) * lds_le[w][tid];
+        for (int w = 0; w < kWaves; ++w) den += __builtin_amdgcn_exp2f(lds_m[w][r] - mx) * lds_le[w][r];
         lse = (mx + __builtin_amdgcn_logf(den)) * kLn2;
       }
-      ws_lse[static_cast<int64_t>(cur.slot) * M + tid] = lse;
+      ws_lse[static_cast<int64_t>(cur.slot) * M + r] = lse;
     }
     __syncthreads();
   }
+}
+
+template <int D, bool FP8, int NB>
+void launch_one(const DecodeParams& p, int num_workers, hipStream_t stream) {
+  const DecodeShape sh = {p.q_len,     p.num_q_heads, p.num_kv_heads, p.group,
+                          p.rows,      p.page_size,   p.bt_stride,    p.tile_tokens,
+                          p.request_split, p.qk_scale_log2};
+  hipLaunchKernelGGL((decode_partial_kernel<D, FP8, NB>), dim3(num_workers),
+                     dim3(Cfg<D, FP8, NB>::kThreads), 0, stream, p.q, p.k_cache, p.v_cache,
+                     p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items, p.worker_offsets,
+                     p.tile_tokens_dev, p.ws_o, p.ws_lse, sh);
+}
+
+template <int D, bool FP8>
+void launch_rows(const DecodeParams& p, int num_workers, hipStream_t stream) {
+  if (p.rows <= 16)
+    launch_one<D, FP8, 1>(p, num_workers, stream);
+  else if (p.rows <= 32)
+    launch_one<D, FP8, 2>(p, num_workers, stream);
+  else
+    launch_one<D, FP8, 4>(p, num_workers, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeParams& p, int head_dim, bool fp8, int num_workers,
                                  hipStream_t stream) {
-  const dim3 grid(num_workers), block(kThreads);
-  const DecodeShape sh = {p.q_len,     p.num_q_heads, p.num_kv_heads, p.group,
-                          p.rows,      p.page_size,   p.bt_stride,    p.tile_tokens,
-                          p.request_split, p.qk_scale_log2};
-#define PKV_LAUNCH(DIM, F8)                                                                   \
-  hipLaunchKernelGGL((decode_partial_kernel<DIM, F8>), grid, block, 0, stream, p.q, p.k_cache, \
-                     p.v_cache, p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items,     \
-                     p.worker_offsets, p.tile_tokens_dev, p.ws_o, p.ws_lse, sh)
   if (head_dim == 128) {
     if (fp8)
-      PKV_LAUNCH(128, true);
+      launch_rows<128, true>(p, num_workers, stream);
     else
-      PKV_LAUNCH(128, false);
+      launch_rows<128, false>(p, num_workers, stream);
   } else {
     if (fp8)
-      PKV_LAUNCH(64, true);
+      launch_rows<64, true>(p, num_workers, stream);
     else
-      PKV_LAUNCH(64, false);
+      launch_rows<64, false>(p, num_workers, stream);
   }
-#undef PKV_LAUNCH
   return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@ namespace pkv {
 constexpr int kDecodeWaves = 8;
 // Decode workgroups resident per compute unit that the default worker count assumes.
 constexpr int kDecodeGroupsPerCU = 1;
-// Largest M = G * Tq one work item may carry (one MFMA column block).
-constexpr int kMaxRows = 16;
+// Largest M = G * Tq one work item may carry (four MFMA column blocks).
+constexpr int kMaxRows = 64;
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B, Tq, Hq, D]

@@ -95,7 +95,7 @@ def test_plan_of_empty_batch():
     (dict(kv_format="fp8", page_size=16), pkv.PKV_ERR_UNSUPPORTED),
     (dict(num_q_heads=6, num_kv_heads=4), pkv.PKV_ERR_UNSUPPORTED),
     (dict(q_len=5), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(num_q_heads=32, num_kv_heads=4, q_len=4), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=1, q_len=4), pkv.PKV_ERR_UNSUPPORTED),  # M = 128 > 64
     (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
     (dict(num_workers=0), pkv.PKV_ERR_INVALID_ARG),
     (dict(tile_tokens=-16), pkv.PKV_ERR_INVALID_ARG),

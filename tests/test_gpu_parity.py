@@ -109,6 +109,27 @@ SMALL = [
          sl=[2, 48, 97, 2000, 4801], T=0, W=9),
     dict(id="fp8_d64_spec4_g4", c=cfg(kv_format="fp8", page_size=64, head_dim=64, q_len=4),
          sl=[4, 5, 63, 64, 65, 67, 130, 1000, 4097], T=128, W=6),
+    # More than 16 rows per kv head (two or four MFMA column blocks):
+    dict(id="g8_spec3_m24", c=cfg(num_q_heads=16, q_len=3), sl=[3, 4, 17, 33, 100, 1000], T=64, W=5),
+    dict(id="g8_spec4_m32", c=cfg(num_q_heads=16, q_len=4), sl=[4, 5, 6, 7, 64, 65, 300, 2049], T=0, W=7),
+    dict(id="g5_spec4_m20_p48", c=cfg(num_q_heads=10, page_size=48, q_len=4), sl=[4, 47, 48, 49, 500],
+         T=96, W=3),
+    dict(id="g16_spec4_m64", c=cfg(num_q_heads=32, q_len=4), sl=[4, 5, 6, 7, 35, 129, 777, 3000], T=64, W=6),
+    dict(id="g12_spec3_m36_d64", c=cfg(num_q_heads=24, head_dim=64, q_len=3), sl=[3, 16, 31, 250, 1500],
+         T=0, W=5),
+    dict(id="g16_spec3_m48_p32", c=cfg(num_q_heads=32, page_size=32, q_len=3), sl=[3, 32, 33, 97, 2000],
+         T=128, W=4),
+    dict(id="g64_m64", c=cfg(num_q_heads=64, num_kv_heads=1), sl=[1, 2, 100, 5000], T=256, W=9),
+    dict(id="g32_spec2_m64_d64_p64", c=cfg(num_q_heads=64, num_kv_heads=2, head_dim=64, page_size=64, q_len=2),
+         sl=[2, 64, 65, 1234], T=0, W=4),
+    dict(id="fp8_g8_spec4_m32", c=cfg(kv_format="fp8", page_size=64, num_q_heads=16, q_len=4),
+         sl=[4, 64, 65, 66, 67, 200, 2049], T=64, W=5),
+    dict(id="fp8_g16_spec4_m64", c=cfg(kv_format="fp8", page_size=64, num_q_heads=32, q_len=4),
+         sl=[4, 5, 64, 67, 129, 1000, 4097], T=0, W=6),
+    dict(id="fp8_g16_spec3_m48_d64", c=cfg(kv_format="fp8", page_size=64, head_dim=64, num_q_heads=32, q_len=3),
+         sl=[3, 66, 700, 3001], T=128, W=3),
+    dict(id="fp8_g12_spec2_m24", c=cfg(kv_format="fp8", page_size=64, num_q_heads=24, q_len=2),
+         sl=[2, 63, 64, 65, 1500], T=0, W=4),
 ]
 
 
@@ -136,6 +157,49 @@ def test_full_size_workloads(name):
     check(inp, out, lse, tag=name)
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,q_len,heads", [("long", 4, (64, 8)), ("fp8_spec", 4, (64, 4))])
+def test_full_size_wide_groups(name, q_len, heads):
+    """A workload's shape with more than 16 rows per kv head: the long workload's
+    64 q / 8 kv heads with four draft tokens (32 rows), and the fp8 workload with 64 q /
+    4 kv heads (64 rows) at 8 requests; default launch, every group against the oracle."""
+    import torch
+    c = dict(synth.ALL[name], q_len=q_len, num_q_heads=heads[0], num_kv_heads=heads[1])
+    if name == "fp8_spec":
+        c["batch"] = 8
+    log("full-size wide %s: generating inputs" % name)
+    inp = synth.make_inputs(c, seed=0)
+    out, lse, _ = run_decode(inp)
+    check(inp, out, lse, tag="%s Tq=%d %dq/%dkv" % ((name, q_len) + heads))
+    del inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("keys", [2, 3, 4])
+@pytest.mark.parametrize("G", [1, 16, 64])
+def test_few_key_rows_worst_rounding(keys, G):
+    """Rows that see 2-4 keys with the inputs a float32 model of the kernel's rounding
+    finds worst for bf16 weights (tests/decode_rounding.py): 64 requests of L = keys,
+    q = e_0 in every query head, key j = a_j e_0, every head dim of value j = v_j.
+    Without the low part of P these rows exceed the 1e-2 contract in the model; the
+    kernel must meet it (G = 1, 16 take one MFMA column block, 64 four)."""
+    from tests.decode_rounding import search_rows
+    r = search_rows(float(1.0 / np.sqrt(128.0)), keys=keys, samples=300_000, seed=keys)
+    n = len(r["a"])
+    inp = synth.make_inputs(cfg(num_q_heads=G, num_kv_heads=1), seed=3, seq_lens=[keys] * n)
+    inp.q[:] = 0
+    inp.q[:, :, :, 0] = synth.f32_to_bf16_bits(np.float32(1.0))
+    for i in range(n):
+        page = inp.block_table[i, 0]
+        inp.k_cache[page, 0, :keys, :] = 0
+        inp.k_cache[page, 0, :keys, 0] = synth.f32_to_bf16_bits(r["a"][i].astype(np.float32))
+        inp.v_cache[page, 0, :keys, :] = synth.f32_to_bf16_bits(r["v"][i].astype(np.float32))[:, None]
+    log("few-key rows: %d keys, G=%d; model without the low part: worst error %.3e" % (
+        keys, G, r["err_plain"].max()))
+    out, lse, _ = run_decode(inp)
+    assert (out == out[:, :, :1, :1]).all()     # every head and dim of a request agrees
+    check(inp, out, lse, tag="few keys %d G %d" % (keys, G))
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
