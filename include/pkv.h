@@ -264,6 +264,27 @@ int pkv_combine_split(const void* workspace, size_t workspace_bytes, int64_t num
                       int num_kv_heads, int head_dim, int request_split, void* out,
                       float* lse_out, void* stream);
 
+/* Bytes of the device array pkv_decode_noalloc keeps on each GPU it runs on. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): one whole decode step,
+ * pkv_decode_partial followed by pkv_combine on `stream`, with the split-KV partials
+ * held in a library-owned device array of PKV_NOALLOC_SCRATCH_BYTES on each GPU
+ * (kept until the process ends) instead of args->workspace, which is ignored (may be
+ * NULL, with workspace_bytes 0). Every other argument is as for pkv_decode_partial
+ * (args->struct_size must be sizeof(pkv_decode_args)); out and lse_out (may be NULL)
+ * as for pkv_combine. The stream must belong to the current device. Makes no
+ * allocation of any kind and runs no PKV_VALIDATE checks. All calls on one GPU share
+ * that GPU's array: calls that overlap on one GPU (concurrent streams or threads)
+ * race. Enqueue only; no sync.
+ * Errors: as pkv_decode_partial and pkv_combine; WORKSPACE when
+ * pkv_workspace_bytes(num_partials, M, D) exceeds PKV_NOALLOC_SCRATCH_BYTES (nothing
+ * enqueued); HIP when the array's address cannot be obtained.
+ */
+int pkv_decode_noalloc(const pkv_decode_args* args, void* out, float* lse_out, void* stream);
+
 /*
  * Block-sparse decode (the HALOps review's sparse attention: a precomputed block mask,
  * masked-out KV tiles skipped, per-tile FP8 scaling kept). The mask has one byte per

@@ -145,6 +145,8 @@ def _load():
         "pkv_prefill_plan_size": (ctypes.c_int, [ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int, _i64p]),
         "pkv_prefill_plan": (ctypes.c_int, [ctypes.c_int, _i32p, _i32p, ctypes.c_int, ctypes.c_int, _i32p]),
         "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]),
+        "pkv_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]),
         "pkv_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -304,12 +306,11 @@ def pkv_workspace_bytes(num_partials, rows_per_partial, head_dim):
     return out.value
 
 
-def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, worker_offsets,
-                       req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
-                       batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
-                       kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
-                       tile_tokens_dev=None, request_split=1, stream=None):
-    """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses."""
+def _decode_args(*, q, k_cache, v_cache, block_table, seq_lens, items, worker_offsets,
+                 req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
+                 batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
+                 kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
+                 tile_tokens_dev=None, request_split=1):
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
     a.q, a.k_cache, a.v_cache = _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
@@ -326,7 +327,26 @@ def pkv_decode_partial(*, q, k_cache, v_cache, block_table, seq_lens, items, wor
     a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
     a.tile_tokens_dev = _ptr(tile_tokens_dev, "tile_tokens_dev")
     a.request_split = request_split
+    return a
+
+
+def pkv_decode_partial(*, stream=None, **kw):
+    """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses
+    (keywords as the fields of pkv_decode_args)."""
+    a = _decode_args(**kw)
     _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def pkv_decode_noalloc(*, out, lse_out=None, stream=None, workspace=None, workspace_bytes=0, **kw):
+    """Enqueue a whole decode step (partials + combine) whose partials live in the
+    library's own device array (no workspace, no allocation); keywords as for
+    pkv_decode_partial, plus out / lse_out as for pkv_combine."""
+    a = _decode_args(workspace=workspace, workspace_bytes=workspace_bytes, **kw)
+    _check(_lib.pkv_decode_noalloc(ctypes.byref(a), _ptr(out, "out"), _ptr(lse_out, "lse_out"),
+                                   _stream_handle(stream)), "pkv_decode_noalloc")
 
 
 def pkv_plan_device_scratch_bytes(batch, num_kv_heads, page_size, kv_format, tile_tokens,

@@ -20,7 +20,7 @@ PROBE_SRC = "read_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
 SOURCES = ["planner.cpp", "api.cpp", "validate.cpp", "decode_partial.hip", "combine.hip", "plan_device.hip",
-           "block_sparse.hip", "kv_append.hip", "prefill.hip"]
+           "block_sparse.hip", "kv_append.hip", "prefill.hip", "noalloc.hip"]
 HEADERS = ["planner.hpp", "kernels.hpp", "status.hpp", "validate.hpp"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

@@ -11,10 +11,18 @@
 
 namespace pkv {
 
+namespace {
+thread_local bool t_validate_off = false;
+}  // namespace
+
 bool validate_enabled() {
+  if (t_validate_off) return false;
   const char* e = std::getenv("PKV_VALIDATE");
   return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
 }
+
+ValidateOff::ValidateOff() : prev_(t_validate_off) { t_validate_off = true; }
+ValidateOff::~ValidateOff() { t_validate_off = prev_; }
 
 namespace {
 

@@ -14,6 +14,19 @@ namespace pkv {
 
 bool validate_enabled();
 
+// While one of these lives, validate_enabled() is false on this thread (entry points
+// that must not allocate, even host memory, run without the checks).
+class ValidateOff {
+ public:
+  ValidateOff();
+  ~ValidateOff();
+  ValidateOff(const ValidateOff&) = delete;
+  ValidateOff& operator=(const ValidateOff&) = delete;
+
+ private:
+  bool prev_;
+};
+
 // seq_lens in [max(1, q_len), bt_stride * P], the block-table entries of every used
 // page in [0, num_pages), and the work list: worker offsets ascending from 0 to at
 // most num_items, n_b = ceil(L_b / T) tiles per request in req_tile_base, and every

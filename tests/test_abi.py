@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -423,3 +423,18 @@ def test_combine_argument_errors(kw, status):
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_combine(**base)
     assert e.value.status == status
+
+
+def test_noalloc_rejects_partials_past_its_array():
+    """pkv_decode_noalloc refuses, before any HIP call, a step whose partials would not
+    fit the library's static device array."""
+    import ctypes
+    a = pkv.DecodeArgs()
+    a.struct_size = ctypes.sizeof(pkv.DecodeArgs)
+    a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 1, 1, 32, 8, 128
+    a.page_size, a.kv_format, a.tile_tokens, a.num_workers = 16, 0, 16, 1
+    # 4 rows x (128 + 1) floats per partial: 2^15 partials need 64.5 MiB + alignment
+    a.num_items = a.num_partials = 1 << 15
+    st = pkv._lib.pkv_decode_noalloc(ctypes.byref(a), None, None, None)
+    assert st == pkv.PKV_ERR_WORKSPACE
+    assert "static scratch" in pkv.pkv_last_error()
