@@ -185,7 +185,22 @@ struct ItemCtx {
   int64_t head_off;                // byte offset of kv head g inside a page
   int64_t page_bytes;              // bytes of one page (all heads)
   int tile_start, tile_end, page_size, row_bytes;
+  unsigned page_magic;             // ceil(2^32 / page_size)
 };
+
+// Page of token j (0 <= j < 2^31) and j's row inside it, without a division: with
+// m = ceil(2^32 / P) the estimate floor(j m / 2^32) exceeds j / P by less than 1/2,
+// so it is the quotient or one more.
+__device__ __forceinline__ int page_of(int j, unsigned magic, int P, int* row) {
+  int q = static_cast<int>(__umulhi(static_cast<unsigned>(j), magic));
+  int r = j - q * P;
+  if (r < 0) {
+    q -= 1;
+    r += P;
+  }
+  *row = r;
+  return q;
+}
 
 // Byte offsets of the two 16-token halves of a chunk (wave-uniform; the block-table
 // reads are scalar loads). A half past the tile end re-reads half 0 (masked later).
@@ -199,16 +214,24 @@ struct HalfOffsets {
 __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chunk) {
   HalfOffsets r;
   const int j0 = it.tile_start + 32 * chunk;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int jh = j0 + 16 * h;
-    if (jh >= it.tile_end) jh = j0;
-    const int page = jh / it.page_size;
-    const int64_t phys = it.bt[page];
-    if (h == 0) r.phys0 = phys;
-    r.off[h] = phys * it.page_bytes + it.head_off +
-               static_cast<int64_t>(jh - page * it.page_size) * it.row_bytes;
+  // Both block-table entries are read before either is used (two scalar loads in
+  // flight at once). Half 1 lies in half 0's page or the next one.
+  int row0, row1;
+  const int page0 = page_of(j0, it.page_magic, it.page_size, &row0);
+  int page1 = page0;
+  row1 = row0;
+  if (j0 + 16 < it.tile_end) {
+    row1 = row0 + 16;
+    if (row1 >= it.page_size) {
+      row1 -= it.page_size;
+      page1 += 1;
+    }
   }
+  const int64_t phys0 = it.bt[page0];
+  const int64_t phys1 = it.bt[page1];
+  r.phys0 = phys0;
+  r.off[0] = phys0 * it.page_bytes + it.head_off + static_cast<int64_t>(row0) * it.row_bytes;
+  r.off[1] = phys1 * it.page_bytes + it.head_off + static_cast<int64_t>(row1) * it.row_bytes;
   return r;
 }
 
@@ -262,8 +285,7 @@ __device__ __forceinline__ void stage_write(uint8_t* __restrict__ st, const Raw<
       const int row = 16 * h + pos / C::kRowBytes;
       const int unit = (pos % C::kRowBytes) / 16;
       kst[k_slot<D, FP8, NB>(row, unit)] = raw.r[0][h][j];
-      u32x4 v = raw.r[1][h][j];
-      if (valid < 32 && row >= valid) v = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = raw.r[1][h][j];
       if constexpr (FP8) {
         u32x4* dst = reinterpret_cast<u32x4*>(vst + row * C::kVStride + 32 * unit);
         dst[0] = fp8x8_to_f16(v[0], v[1], v_pow2);
@@ -272,6 +294,21 @@ __device__ __forceinline__ void stage_write(uint8_t* __restrict__ st, const Raw<
         *reinterpret_cast<u32x4*>(vst + row * C::kVStride + 16 * unit) = v;
       }
     }
+  if (valid < 32) {  // a tile's last chunk only (wave-uniform): overwrite the tail rows
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        const int pos = j * 1024 + lane * 16;
+        const int row = 16 * h + pos / C::kRowBytes;
+        const int unit = (pos % C::kRowBytes) / 16;
+        if (row >= valid) {
+          u32x4* dst = reinterpret_cast<u32x4*>(vst + row * C::kVStride + (FP8 ? 32 : 16) * unit);
+          dst[0] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (FP8) dst[1] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+  }
 }
 
 // K operands of half h: lane (n, gq) takes bytes 64u + 16gq of token row 16h + n;
@@ -439,7 +476,6 @@ __device__ __forceinline__ void process_chunk(const uint8_t* __restrict__ st, co
       if (__builtin_amdgcn_ballot_w64(low)) {
         // The low part goes through a fresh accumulator and is added in place, so the
         // accumulators keep their registers whichever way this branch goes.
-        __asm__ volatile("");
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           u32x4 pln;
@@ -470,6 +506,7 @@ struct DecodeShape {
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
   int request_split;  // work-list request b is part b % split of the caller's request b / split
   float qk_scale_log2;
+  unsigned page_magic;  // ceil(2^32 / page_size)
 };
 
 // Wave-uniform description of one work item.
@@ -497,6 +534,7 @@ __device__ __forceinline__ ItemInfo item_info(const int32_t* __restrict__ items,
   r.it.tile_start = ti * sh.tile_tokens;
   r.it.tile_end = min(r.L, r.it.tile_start + sh.tile_tokens);
   r.it.page_size = sh.page_size;
+  r.it.page_magic = sh.page_magic;
   r.nchunks = (r.it.tile_end - r.it.tile_start + 31) >> 5;
   return r;
 }
@@ -745,9 +783,12 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
 
 template <int D, bool FP8, int NB>
 void launch_one(const DecodeParams& p, int num_workers, hipStream_t stream) {
+  const unsigned magic =
+      static_cast<unsigned>(((1ull << 32) + static_cast<unsigned>(p.page_size) - 1) /
+                            static_cast<unsigned>(p.page_size));
   const DecodeShape sh = {p.q_len,     p.num_q_heads, p.num_kv_heads, p.group,
                           p.rows,      p.page_size,   p.bt_stride,    p.tile_tokens,
-                          p.request_split, p.qk_scale_log2};
+                          p.request_split, p.qk_scale_log2, magic};
   hipLaunchKernelGGL((decode_partial_kernel<D, FP8, NB>), dim3(num_workers),
                      dim3(Cfg<D, FP8, NB>::kThreads), 0, stream, p.q, p.k_cache, p.v_cache,
                      p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items, p.worker_offsets,
