@@ -44,6 +44,7 @@
  *     q            bf16 [B, Tq, Hq, D]
  *     k/v_cache    bf16 or OCP e4m3fn bytes [num_pages, Hkv, P, D]
  *     k/v_scale    fp32 [num_pages, Hkv]: one scale per physical page and kv head
+ *                  (FP8 with any P; with P = 64 a scale covers a 64-token tile)
  *     block_table  int32 [B, bt_stride]; entry (b, p) is the physical page of
  *                  request b's logical page p; only p < ceil(L_b / P) is read
  *     seq_lens     int32 [B]; L_b counts the Tq draft tokens, which sit at
@@ -70,7 +71,7 @@ enum pkv_kv_format { PKV_KV_BF16 = 0, PKV_KV_FP8_E4M3FN = 1 };
 enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum, ... */
-  PKV_ERR_UNSUPPORTED = -2,  /* D not 64/128; P not a multiple of 16; fp8 with P != 64;
+  PKV_ERR_UNSUPPORTED = -2,  /* D not 64/128; P not a multiple of 16;
                                 Hq % Hkv != 0; Tq not in [1, 4]; M > 64; tile not a
                                 multiple of the quantum */
   PKV_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
@@ -420,8 +421,8 @@ typedef struct pkv_prefill_args {
  * kv_len < n_b or kv_len > bt_stride * P, is skipped and its rows are not written.
  * The softmax scale may be negative (taken exactly); a zero scale acts as the smallest
  * normal float. FP8 page scales must be positive. Enqueue only.
- * Errors: INVALID_ARG, UNSUPPORTED (D not 64/128, P not a multiple of 16, fp8 with
- * P != 64, G not 1, 2 or a multiple of 4), ALIGNMENT (q, out, caches, items 16 bytes),
+ * Errors: INVALID_ARG, UNSUPPORTED (D not 64/128, P not a multiple of 16,
+ * G not 1, 2 or a multiple of 4), ALIGNMENT (q, out, caches, items 16 bytes),
  * HIP.
  */
 int pkv_prefill(const pkv_prefill_args* args, void* stream);

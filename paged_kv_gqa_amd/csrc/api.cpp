@@ -57,9 +57,6 @@ int check_shape(int q_len, int num_q_heads, int num_kv_heads, int head_dim, int 
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (page_size % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
-  if (kv_format == PKV_KV_FP8_E4M3FN && page_size != 64)
-    return fail(PKV_ERR_UNSUPPORTED, "fp8 KV needs page_size 64 (one scale per 64-token tile), got %d",
-                page_size);
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, num_kv_heads);
@@ -588,8 +585,6 @@ int pkv_prefill(const pkv_prefill_args* a, void* stream) {
   if (a->page_size < 16 || a->page_size % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", a->page_size);
   const bool fp8 = a->kv_format == PKV_KV_FP8_E4M3FN;
-  if (fp8 && a->page_size != 64)
-    return fail(PKV_ERR_UNSUPPORTED, "fp8 KV needs page_size 64, got %d", a->page_size);
   int st = check_prefill_heads(a->num_q_heads, a->num_kv_heads);
   if (st != PKV_OK) return st;
   if (a->batch < 0 || a->num_items < 0 || a->num_pages < 0 || a->bt_stride < 1)

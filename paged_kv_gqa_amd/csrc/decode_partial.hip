@@ -31,7 +31,8 @@
 //     each lane four consecutive tokens of one head dimension, the operand layout V^T
 //     needs.
 // - FP8 (OCP e4m3fn) K bytes are widened to bf16 with the gfx950 conversion
-//   instruction (exact) and the page's K scale multiplies the scores. FP8 V bytes are
+//   instruction (exact) and the page's K scale multiplies the scores (one scale per
+//   page and kv head; a 16-token half lies in one page). FP8 V bytes are
 //   converted on their way into LDS to fp16 (code x 2^e, exact: the conversion
 //   instruction applies a power-of-two scale), so P.V runs in fp16; the rest of the
 //   page's V scale, v_scale / 2^e in [1, 2), multiplies P.
@@ -203,12 +204,11 @@ __device__ __forceinline__ int page_of(int j, unsigned magic, int P, int* row) {
 }
 
 // Byte offsets of the two 16-token halves of a chunk (wave-uniform; the block-table
-// reads are scalar loads). A half past the tile end re-reads half 0 (masked later).
-// phys0: physical page of half 0, which holds the whole chunk when pages are 64
-// tokens (fp8), so it also indexes the chunk's page scales.
+// reads are scalar loads) and their physical pages, which index the FP8 page scales.
+// A half past the tile end re-reads half 0 (masked later).
 struct HalfOffsets {
   int64_t off[2];
-  int64_t phys0;
+  int64_t phys[2];
 };
 
 __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chunk) {
@@ -229,7 +229,8 @@ __device__ __forceinline__ HalfOffsets chunk_offsets(const ItemCtx& it, int chun
   }
   const int64_t phys0 = it.bt[page0];
   const int64_t phys1 = it.bt[page1];
-  r.phys0 = phys0;
+  r.phys[0] = phys0;
+  r.phys[1] = phys1;
   r.off[0] = phys0 * it.page_bytes + it.head_off + static_cast<int64_t>(row0) * it.row_bytes;
   r.off[1] = phys1 * it.page_bytes + it.head_off + static_cast<int64_t>(row1) * it.row_bytes;
   return r;
@@ -269,11 +270,11 @@ __device__ __forceinline__ int k_slot(int row, int unit) {
 
 // Stage a loaded chunk. V rows at or past `valid` (tokens past the tile end, which
 // may be unwritten cache memory) are stored as zeros, so that a zero probability
-// never meets a NaN in P.V. FP8 V codes are stored as fp16 code x v_pow2 (a power of
-// two).
+// never meets a NaN in P.V. FP8 V codes of half h are stored as fp16 code x
+// v_pow2[h] (a power of two).
 template <int D, bool FP8, int NB>
 __device__ __forceinline__ void stage_write(uint8_t* __restrict__ st, const Raw<D, FP8, NB>& raw,
-                                            int lane, int valid, float v_pow2) {
+                                            int lane, int valid, const float (&v_pow2)[2]) {
   using C = Cfg<D, FP8, NB>;
   u32x4* const kst = reinterpret_cast<u32x4*>(st);
   uint8_t* const vst = st + C::kKBytes;
@@ -288,8 +289,8 @@ __device__ __forceinline__ void stage_write(uint8_t* __restrict__ st, const Raw<
       const u32x4 v = raw.r[1][h][j];
       if constexpr (FP8) {
         u32x4* dst = reinterpret_cast<u32x4*>(vst + row * C::kVStride + 32 * unit);
-        dst[0] = fp8x8_to_f16(v[0], v[1], v_pow2);
-        dst[1] = fp8x8_to_f16(v[2], v[3], v_pow2);
+        dst[0] = fp8x8_to_f16(v[0], v[1], v_pow2[h]);
+        dst[1] = fp8x8_to_f16(v[2], v[3], v_pow2[h]);
       } else {
         *reinterpret_cast<u32x4*>(vst + row * C::kVStride + 16 * unit) = v;
       }
@@ -347,8 +348,8 @@ struct RowState {
 template <int D, bool FP8, int NB, class QGet>
 __device__ __forceinline__ void process_chunk(const uint8_t* __restrict__ st, const QGet& qget,
                                               f32x4 (&acc)[NB][D / 16], RowState<NB>& rs, int j0,
-                                              const int (&lim)[NB], float c_qk, float p_mul, int n,
-                                              int gq) {
+                                              const int (&lim)[NB], const float (&c_qk)[2],
+                                              const float (&p_mul)[2], int n, int gq) {
   using C = Cfg<D, FP8, NB>;
   constexpr bool kLow = C::kLowPart;
   constexpr bool kEagerLow = kLow && NB > 1;
@@ -388,7 +389,7 @@ __device__ __forceinline__ void process_chunk(const uint8_t* __restrict__ st, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = j0 + 16 * (e >> 2) + 4 * gq + (e & 3);
-      sv[e] = (j < lim[nb]) ? sacc[e >> 2][e & 3] * c_qk : -INFINITY;
+      sv[e] = (j < lim[nb]) ? sacc[e >> 2][e & 3] * c_qk[e >> 2] : -INFINITY;
     }
     const float lane_max = max8(sv);
     const float m_new = fmaxf(rs.m[nb], group_max(lane_max));
@@ -411,7 +412,8 @@ __device__ __forceinline__ void process_chunk(const uint8_t* __restrict__ st, co
     rs.lexact[nb] += pexact;
     if constexpr (FP8) {  // P.V weights carry the V scale's non-power-of-two part
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ph[nb][e] = pack_f16(p[2 * e] * p_mul, p[2 * e + 1] * p_mul);
+      for (int e = 0; e < 4; ++e)
+        ph[nb][e] = pack_f16(p[2 * e] * p_mul[e >> 1], p[2 * e + 1] * p_mul[e >> 1]);
     } else {
       float ps = 0.f;
 #pragma unroll
@@ -581,9 +583,10 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
   constexpr bool kPrefetchQ = NB == 1;
   Raw<D, FP8, NB> raw;
   u32x4 qf_next[kPrefetchQ ? NB : 1][C::kSteps];
-  // FP8: the K and V page scales of the unit in flight, loaded with its K/V so that
-  // their dependent loads (block-table entry, then scale) stay off the compute path.
-  float ksc_next = 1.f, vsc_next = 1.f;
+  // FP8: the K and V page scales of the unit in flight (one per 16-token half, whose
+  // pages may differ), loaded with its K/V so that their dependent loads (block-table
+  // entry, then scale) stay off the compute path.
+  float ksc_next[2] = {1.f, 1.f}, vsc_next[2] = {1.f, 1.f};
   int u_itx = -1, u_c = 0;
   ItemInfo u_info;
   auto find_unit = [&](int from) {  // first unit of this wave in items >= from
@@ -626,9 +629,12 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
     const HalfOffsets ho = chunk_offsets(u_info.it, u_c);
     load_raw<D, FP8, NB>(raw, k_cache, v_cache, ho, lane);
     if constexpr (FP8) {
-      const int64_t sidx = ho.phys0 * sh.num_kv_heads + u_info.g;
-      ksc_next = k_scale[sidx];
-      vsc_next = v_scale[sidx];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t sidx = ho.phys[h] * sh.num_kv_heads + u_info.g;
+        ksc_next[h] = k_scale[sidx];
+        vsc_next[h] = v_scale[sidx];
+      }
     }
     if constexpr (kPrefetchQ) {
       if (u_c == wid) load_q(qf_next, u_info.b, u_info.g);  // first chunk of an item
@@ -692,14 +698,18 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
       // This unit's page scales are used before issue_unit loads the next unit's. The V
       // scale splits into v_pow2 = 2^e, applied exactly when V is converted to fp16,
       // and p_mul = v_scale / 2^e, in [1, 2) while e lies in [-15, 7].
-      float c_qk = sh.qk_scale_log2, p_mul = 1.f, v_pow2 = 1.f;
+      float c_qk[2] = {sh.qk_scale_log2, sh.qk_scale_log2}, p_mul[2] = {1.f, 1.f},
+            v_pow2[2] = {1.f, 1.f};
       if constexpr (FP8) {
-        c_qk *= ksc_next;
-        int e;
-        (void)frexpf(vsc_next, &e);
-        const int e1 = min(max(e - 1, -15), 7);
-        v_pow2 = ldexpf(1.f, e1);
-        p_mul = ldexpf(vsc_next, -e1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          c_qk[h] *= ksc_next[h];
+          int e;
+          (void)frexpf(vsc_next[h], &e);
+          const int e1 = min(max(e - 1, -15), 7);
+          v_pow2[h] = ldexpf(1.f, e1);
+          p_mul[h] = ldexpf(vsc_next[h], -e1);
+        }
       }
       stage_write<D, FP8, NB>(my_stage, raw, lane, cur.it.tile_end - j0, v_pow2);
       if (c + kWaves < cur.nchunks)

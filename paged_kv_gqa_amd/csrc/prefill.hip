@@ -34,8 +34,8 @@
 //   computed (double-buffered stage, one barrier per block); the block-table entries
 //   are fetched one block earlier still.
 // FP8 (e4m3fn) K/V bytes are widened to bf16 exactly when staged, once per workgroup;
-// with 64-token pages a 32-key block lies in one page, so its K scale multiplies the
-// scores and its V scale P.
+// each 16-key half of a block lies in one page, whose K scale multiplies that half's
+// scores and whose V scale its P.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -257,7 +257,7 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
                                              const u32x4 (&qf)[HPW][PCfg<D, FP8>::kSteps],
                                              f32x4 (&acc)[HPW][PCfg<D, FP8>::kDimBlocks],
                                              RowState (&rs)[HPW], bool diag, int j0, int pos, int n,
-                                             int gq, float c, float v_mul) {
+                                             int gq, const float (&c)[2], const float (&v_mul)[2]) {
   using C = PCfg<D, FP8>;
   using S = Stage<D>;
   // K operands: key 16h + n, dims op_dim(s, gq, 0..7).
@@ -294,7 +294,7 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(sacc[hh][e >> 2][e & 3], c, rs[hh].negm);
+    for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(sacc[hh][e >> 2][e & 3], c[e >> 2], rs[hh].negm);
     amax[hh] = max8(arg[hh]);
     raise |= amax[hh] > kRescaleSlack;
   }
@@ -305,7 +305,9 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
       float raw[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) raw[e] = sacc[hh][e >> 2][e & 3];
-      const float mc = group_max(max8(raw)) * c;  // the row's block maximum, log2 units
+      // The row's block maximum in log2 units (c > 0 in both halves).
+      const float mc = group_max(fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])) * c[0],
+                                       fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])) * c[1]));
       // Lanes whose row keeps its maximum multiply by 1 (no divergent branch, so the
       // accumulators are scaled in place).
       const bool up = mc > rs[hh].m + kRescaleSlack;  // the same in the row's four lanes
@@ -316,7 +318,7 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
       rs[hh].m = up ? mc : rs[hh].m;
       rs[hh].negm = up ? -mc : rs[hh].negm;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(raw[e], c, rs[hh].negm);
+      for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(raw[e], c[e >> 2], rs[hh].negm);
       amax[hh] = max8(arg[hh]);
     }
   }
@@ -339,7 +341,7 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
     rs[hh].l += sum;
     if constexpr (FP8) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[hh][e] *= v_mul;
+      for (int e = 0; e < 8; ++e) pv[hh][e] *= v_mul[e >> 2];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) ph[hh][e] = pack_bf16(pv[hh][2 * e], pv[hh][2 * e + 1]);
@@ -456,38 +458,52 @@ void prefill_kernel(const PrefillParams p) {
   block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
   load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, 0, L, tid);
   if (nblocks > 1) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
-  float ksc = 1.f, vsc = 1.f;  // FP8 page scales of the block being computed
-  int scale_page = 0;          // FP8: physical page of the next block
+  // FP8 page scales of the block being computed, one per 16-key half (a half lies in
+  // one page; the two may differ when pages are shorter than 32 keys or not aligned to
+  // blocks), and the physical pages of the next block's halves.
+  float ksc[2] = {1.f, 1.f}, vsc[2] = {1.f, 1.f};
+  int scale_page[2] = {0, 0};
+  auto half_page = [&](int j) { return bt[min(j, L - 1) / p.page_size]; };
   if constexpr (FP8) {
-    const int64_t sidx = static_cast<int64_t>(bt[0]) * p.num_kv_heads + g;
-    ksc = p.k_scale[sidx];
-    vsc = p.v_scale[sidx];
-    scale_page = bt[min(kBlockKeys, L - 1) / p.page_size];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t sidx = static_cast<int64_t>(half_page(16 * h)) * p.num_kv_heads + g;
+      ksc[h] = p.k_scale[sidx];
+      vsc[h] = p.v_scale[sidx];
+      scale_page[h] = half_page(kBlockKeys + 16 * h);
+    }
   }
   for (int kb = 0; kb < nblocks; ++kb) {
     Stage<D>& st = stage[kb & 1];
     stage_block<D, FP8, NT>(st, regs, tid);
     __syncthreads();
-    float ksc_next = 1.f, vsc_next = 1.f;
+    float ksc_next[2] = {1.f, 1.f}, vsc_next[2] = {1.f, 1.f};
     if (kb + 1 < nblocks) {
       load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, kb + 1, L, tid);
       if (kb + 2 < nblocks) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
       if constexpr (FP8) {
-        const int64_t sidx = static_cast<int64_t>(scale_page) * p.num_kv_heads + g;
-        ksc_next = p.k_scale[sidx];
-        vsc_next = p.v_scale[sidx];
-        if (kb + 2 < nblocks) scale_page = bt[min((kb + 2) * kBlockKeys, L - 1) / p.page_size];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t sidx = static_cast<int64_t>(scale_page[h]) * p.num_kv_heads + g;
+          ksc_next[h] = p.k_scale[sidx];
+          vsc_next[h] = p.v_scale[sidx];
+          if (kb + 2 < nblocks) scale_page[h] = half_page((kb + 2) * kBlockKeys + 16 * h);
+        }
       }
     }
     if (kb < wave_blocks) {
       const int j0 = kb * kBlockKeys;
       // c > 0 keeps masked keys at a = -inf (a zero scale acts as the smallest normal one).
-      const float c = fmaxf(qk_log2 * ksc, 1.17549435e-38f);
+      const float c[2] = {fmaxf(qk_log2 * ksc[0], 1.17549435e-38f),
+                          fmaxf(qk_log2 * ksc[1], 1.17549435e-38f)};
       attend_block<D, FP8, HPW>(st, qf, acc, rs, j0 + kBlockKeys - 1 > wave_first_pos, j0, pos, n,
                                 gq, c, vsc);
     }
-    ksc = ksc_next;
-    vsc = vsc_next;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ksc[h] = ksc_next[h];
+      vsc[h] = vsc_next[h];
+    }
   }
 
   // Rows to the output: lane (n, gq) holds dims 16bl + 4gq + v of query n; the row's

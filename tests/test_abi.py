@@ -75,8 +75,6 @@ def test_plan_matches_reference_on_workloads(name, W):
        st.sampled_from([16, 32, 64]), st.integers(1, 40), st.integers(0, 6), st.sampled_from(["bf16", "fp8"]),
        st.integers(1, 4))
 def test_plan_matches_reference_fuzz(sl, Hkv, P, W, k, fmt, q_len):
-    if fmt == "fp8":
-        P = 64
     sl = [max(L, q_len) for L in sl]
     T = 0 if k == 0 else ref_plan.tile_quantum(P, fmt) * k
     assert_same_plan(sl, q_len, Hkv * min(4, 16 // q_len), Hkv, 128, P, fmt, T, W)
@@ -92,7 +90,6 @@ def test_plan_of_empty_batch():
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
     (dict(page_size=24), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(kv_format="fp8", page_size=16), pkv.PKV_ERR_UNSUPPORTED),
     (dict(num_q_heads=6, num_kv_heads=4), pkv.PKV_ERR_UNSUPPORTED),
     (dict(q_len=5), pkv.PKV_ERR_UNSUPPORTED),
     (dict(num_q_heads=32, num_kv_heads=1, q_len=4), pkv.PKV_ERR_UNSUPPORTED),  # M = 128 > 64
@@ -156,7 +153,7 @@ def decode_kwargs(**kw):
     (dict(workspace_bytes=100), pkv.PKV_ERR_WORKSPACE),
     (dict(head_dim=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(tile_tokens=24), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),     # tile 32: the fp8 quantum is lcm(16, 64)
     (dict(kv_format="fp8", page_size=64, tile_tokens=64), pkv.PKV_ERR_INVALID_ARG),  # no scales
     (dict(k_scale=10 * A), pkv.PKV_ERR_INVALID_ARG),                                  # bf16 with scales
     (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
@@ -258,7 +255,6 @@ def plan_device_kwargs(**kw):
     (dict(tile_tokens=-16), pkv.PKV_ERR_INVALID_ARG),
     (dict(tile_tokens=(1 << 18) + 16), pkv.PKV_ERR_UNSUPPORTED),
     (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),          # fp8 needs page size 64
     (dict(info=None), pkv.PKV_ERR_INVALID_ARG),
     (dict(seq_lens=None), pkv.PKV_ERR_INVALID_ARG),
     (dict(items=2 * A + 4), pkv.PKV_ERR_ALIGNMENT),
@@ -363,7 +359,7 @@ def prefill_kwargs(**kw):
     (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
     (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
     (dict(page_size=8), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(kv_format="fp8"), pkv.PKV_ERR_UNSUPPORTED),                  # fp8 needs page 64
+    (dict(kv_format="fp8"), pkv.PKV_ERR_INVALID_ARG),                  # no scales (page 16)
     (dict(kv_format="fp8", page_size=64), pkv.PKV_ERR_INVALID_ARG),    # no scales
     (dict(num_q_heads=6), pkv.PKV_ERR_UNSUPPORTED),                    # G = 3
     (dict(items=5 * A + 4), pkv.PKV_ERR_ALIGNMENT),

@@ -96,6 +96,8 @@ SMALL = [
          keep=0.4, T=96, W=5),
     dict(id="fp8_d64_spec4_keep60", c=cfg(kv_format="fp8", page_size=64, head_dim=64, q_len=4),
          keep=0.6, T=0, W=0),
+    dict(id="fp8_p16_spec2_keep40", c=cfg(kv_format="fp8", page_size=16, q_len=2), keep=0.4, T=64, W=5),
+    dict(id="fp8_p32_spec4_keep50", c=cfg(kv_format="fp8", page_size=32, q_len=4), keep=0.5, T=0, W=0),
 ]
 LENS = [1, 16, 17, 63, 64, 65, 200, 777, 1500, 3000]
 

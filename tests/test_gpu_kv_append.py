@@ -92,6 +92,9 @@ CASES = [
     dict(id="fp8_t2_rope", c=cfg(kv_format="fp8", page_size=64, q_len=2), rope=True),
     dict(id="fp8_t4_rope_g4", c=cfg(kv_format="fp8", page_size=64, q_len=4, num_q_heads=16, num_kv_heads=4), rope=True),
     dict(id="fp8_t3_d64", c=cfg(kv_format="fp8", page_size=64, q_len=3, head_dim=64), rope=False),
+    dict(id="fp8_p16_t4_rope", c=cfg(kv_format="fp8", page_size=16, q_len=4), rope=True),
+    dict(id="fp8_p32_t2", c=cfg(kv_format="fp8", page_size=32, q_len=2), rope=False),
+    dict(id="fp8_p48_t3_rope_d64", c=cfg(kv_format="fp8", page_size=48, q_len=3, head_dim=64), rope=True),
 ]
 # lengths hitting fresh pages (L - Tq on a page boundary), page-spanning new tokens,
 # and pages with earlier tokens

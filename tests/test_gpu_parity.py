@@ -130,6 +130,16 @@ SMALL = [
          sl=[3, 66, 700, 3001], T=128, W=3),
     dict(id="fp8_g12_spec2_m24", c=cfg(kv_format="fp8", page_size=64, num_q_heads=24, q_len=2),
          sl=[2, 63, 64, 65, 1500], T=0, W=4),
+    # FP8 with pages shorter than 64 tokens (one scale per page; a 32-token chunk
+    # spans two 16-token pages) and pages not aligned to chunks (48):
+    dict(id="fp8_p16_spec4", c=cfg(kv_format="fp8", page_size=16, q_len=4),
+         sl=[4, 15, 16, 17, 33, 100, 257, 1000], T=64, W=7),
+    dict(id="fp8_p32_g8_spec2", c=cfg(kv_format="fp8", page_size=32, num_q_heads=16, q_len=2),
+         sl=[2, 31, 32, 33, 500, 2049], T=0, W=5),
+    dict(id="fp8_p48_d64", c=cfg(kv_format="fp8", page_size=48, head_dim=64),
+         sl=[1, 47, 48, 49, 95, 97, 700], T=192, W=3),
+    dict(id="fp8_p16_g16_spec4_m64", c=cfg(kv_format="fp8", page_size=16, num_q_heads=32, q_len=4),
+         sl=[4, 17, 64, 129, 1500], T=128, W=4),
 ]
 
 

@@ -95,6 +95,11 @@ SMALL = [
          q=[1, 64, 65, 190], pre=[0, 1, 63, 129]),
     dict(id="fp8_g1_d128", c=cfg(kv_format="fp8", page_size=64, num_q_heads=2), q=[33, 300],
          pre=[500, 0]),
+    dict(id="fp8_g4_d128_p16", c=cfg(kv_format="fp8", page_size=16), q=[70, 5, 128], pre=[0, 17, 60]),
+    dict(id="fp8_g2_d64_p48", c=cfg(kv_format="fp8", page_size=48, head_dim=64, num_q_heads=4),
+         q=[1, 47, 49, 190], pre=[0, 1, 95, 129]),
+    dict(id="fp8_g8_d128_p32", c=cfg(kv_format="fp8", page_size=32, num_q_heads=8), q=[100, 33],
+         pre=[31, 300]),
 ]
 
 

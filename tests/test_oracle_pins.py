@@ -84,6 +84,7 @@ def torch_dense_reference(inp):
     dict(num_q_heads=2, num_kv_heads=2),                          # G = 1: plain MHA
     dict(q_len=4, seq_lens=(4, 17, 66)),                          # causal draft rows
     dict(kv_format="fp8", page_size=64, seq_lens=(64, 65, 130), q_len=2),
+    dict(kv_format="fp8", page_size=16, seq_lens=(15, 17, 130), q_len=3),   # a scale per 16-token page
     dict(head_dim=64, page_size=32, num_q_heads=8, num_kv_heads=1),
 ])
 def test_matches_torch_sdpa(kw):
