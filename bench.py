@@ -462,6 +462,9 @@ def main():
     else:
         plan = runner.last_plan
         step_desc = "host plan (read in place by the kernels) + decode_partial + combine"
+        if plan["N"] == inp.batch * inp.num_kv_heads and mask_h is None:
+            step_desc = ("host plan (read in place by the kernels) + decode_partial (one tile per "
+                         "request: it writes the final rows, no combine)")
     if mask_h is not None:
         step_desc = "block mask compaction + " + step_desc
     if args.append:

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 /* KV element formats. FP8 is OCP e4m3fn (bias 7, max 448, no infinities). */
 enum pkv_kv_format { PKV_KV_BF16 = 0, PKV_KV_FP8_E4M3FN = 1 };
@@ -175,6 +175,14 @@ typedef struct pkv_decode_args {
    * is [batch / V, Tq, V * num_q_heads, D]. Block-sparse decode uses V = Hkv with one
    * kv head per part (see pkv_block_sparse_compact); V = 1 is the layout above. */
   int request_split;
+  /* ABI 3 (optional; a struct_size ending before these fields means NULL). When out is
+   * non-NULL (bf16 [B, Tq, Hq, D], 16-byte aligned; request_split must be 1), the
+   * items of requests cut into a single tile (L_b <= T) also write their rows' final
+   * output and, if lse_out is non-NULL (fp32 [B, Tq, Hq]), log-sum-exp there, bit for
+   * bit what pkv_combine would write for them. When every request of the plan is a
+   * single tile (num_items == B * Hkv), the combine can then be skipped. */
+  void* out;
+  float* lse_out;
 } pkv_decode_args;
 
 /*

@@ -67,6 +67,7 @@ class DecodeArgs(ctypes.Structure):
         ("bt_stride", ctypes.c_int), ("kv_format", ctypes.c_int), ("tile_tokens", ctypes.c_int),
         ("num_workers", ctypes.c_int), ("scale", ctypes.c_float),
         ("tile_tokens_dev", ctypes.c_void_p), ("request_split", ctypes.c_int),
+        ("out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p),
     ]
 
 
@@ -310,7 +311,7 @@ def _decode_args(*, q, k_cache, v_cache, block_table, seq_lens, items, worker_of
                  req_tile_base, workspace, workspace_bytes, num_items, num_partials, num_pages,
                  batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, bt_stride,
                  kv_format, tile_tokens, num_workers, scale, k_scale=None, v_scale=None,
-                 tile_tokens_dev=None, request_split=1):
+                 tile_tokens_dev=None, request_split=1, direct_out=None, direct_lse_out=None):
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
     a.q, a.k_cache, a.v_cache = _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
@@ -327,12 +328,15 @@ def _decode_args(*, q, k_cache, v_cache, block_table, seq_lens, items, worker_of
     a.tile_tokens, a.num_workers, a.scale = tile_tokens, num_workers, scale
     a.tile_tokens_dev = _ptr(tile_tokens_dev, "tile_tokens_dev")
     a.request_split = request_split
+    a.out = _ptr(direct_out, "direct_out")
+    a.lse_out = _ptr(direct_lse_out, "direct_lse_out")
     return a
 
 
 def pkv_decode_partial(*, stream=None, **kw):
     """Enqueue the split-KV partial kernel. Device arguments are tensors or raw addresses
-    (keywords as the fields of pkv_decode_args)."""
+    (keywords as the fields of pkv_decode_args; its optional out / lse_out are
+    direct_out / direct_lse_out here)."""
     a = _decode_args(**kw)
     _check(_lib.pkv_decode_partial(ctypes.byref(a), _stream_handle(stream)), "pkv_decode_partial")
 
@@ -865,13 +869,21 @@ class PagedDecode:
                            page_size=self.page_size, bt_stride=bt_stride,
                            kv_format=self.kv_format, tile_tokens=p["T"], num_workers=p["W"],
                            scale=scale, k_scale=k_scale, v_scale=v_scale, tile_tokens_dev=tile_dev,
-                           request_split=prob["split"], stream=sh)
+                           request_split=prob["split"],
+                           direct_out=out if prob["split"] == 1 else None,
+                           direct_lse_out=lse_out if prob["split"] == 1 else None, stream=sh)
         if partial_events is not None:
             partial_events[1].record()
-        pkv_combine_split(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
-                          req_tile_base=p["req_tile_base"], batch=prob["batch"], q_len=self.q_len,
-                          num_q_heads=prob["Hq"], num_kv_heads=prob["Hkv"], head_dim=self.head_dim,
-                          request_split=prob["split"], out=out, lse_out=lse_out, stream=sh)
+        # A host plan with one tile per request leaves nothing to merge: decode_partial
+        # has already written every final row (the combine would rewrite the same bits).
+        single = (not use_device_plan and prob["split"] == 1
+                  and p["N"] == prob["batch"] * prob["Hkv"])
+        if not single:
+            pkv_combine_split(workspace=ws, workspace_bytes=ws_bytes, num_partials=p["NP"],
+                              req_tile_base=p["req_tile_base"], batch=prob["batch"], q_len=self.q_len,
+                              num_q_heads=prob["Hq"], num_kv_heads=prob["Hkv"],
+                              head_dim=self.head_dim, request_split=prob["split"], out=out,
+                              lse_out=lse_out, stream=sh)
         k = p["slot"]
         if k is not None:
             if self._consumed[k] is None:

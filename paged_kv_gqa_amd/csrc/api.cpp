@@ -186,6 +186,9 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
       a->struct_size >= offsetof(pkv_decode_args, tile_tokens_dev) + sizeof(a->tile_tokens_dev);
   const bool has_split =
       a->struct_size >= offsetof(pkv_decode_args, request_split) + sizeof(a->request_split);
+  const bool has_out = a->struct_size >= offsetof(pkv_decode_args, lse_out) + sizeof(a->lse_out);
+  void* const direct_out = has_out ? a->out : nullptr;
+  float* const direct_lse = has_out ? a->lse_out : nullptr;
   const int32_t* tile_dev = has_tile_dev ? a->tile_tokens_dev : nullptr;
   const int split = (has_split && a->request_split != 0) ? a->request_split : 1;
   int st = check_shape(a->q_len, a->num_q_heads, a->num_kv_heads, a->head_dim, a->page_size,
@@ -226,6 +229,13 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   if (a->workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes, need);
   if (!std::isfinite(a->scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (direct_out == nullptr && direct_lse != nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "lse_out without out");
+  if (direct_out != nullptr && split != 1)
+    return fail(PKV_ERR_INVALID_ARG, "out needs request_split 1");
+  if ((direct_out != nullptr && !aligned(direct_out, 16)) ||
+      (direct_lse != nullptr && !aligned(direct_lse, 4)))
+    return fail(PKV_ERR_ALIGNMENT, "out must be 16-byte aligned, lse_out 4-byte");
 
   pkv::DecodeParams p;
   p.q = static_cast<const uint16_t*>(a->q);
@@ -252,6 +262,8 @@ int pkv_decode_partial(const pkv_decode_args* a, void* stream) {
   p.tile_tokens_dev = tile_dev;
   p.request_split = split;
   p.qk_scale_log2 = a->scale * kLog2e;
+  p.out = static_cast<uint16_t*>(direct_out);
+  p.lse_out = direct_lse;
   if (pkv::validate_enabled()) {
     st = pkv::validate_decode(a, tile_dev, static_cast<hipStream_t>(stream));
     if (st != PKV_OK) return st;

@@ -6,8 +6,8 @@
 // each lane forms w_i = exp(lse_i - max). The partial outputs are then accumulated
 // in split order with the weights broadcast from their lanes; their loads do not
 // depend on each other, so several are in flight at once. Fixed summation order
-// keeps the result deterministic. A request with a single tile still passes through
-// here (its partial is already normalised; the merge only casts it to bf16).
+// keeps the result deterministic. A request with a single tile is copied (its partial
+// is already normalised: the output is cast to bf16, the lse passed through).
 #include "kernels.hpp"
 
 #include <math.h>
@@ -54,6 +54,25 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
   const float* o = p.ws_o + (slot0 * p.rows + r) * D + E * lane;  // stride rows * D per split
   const int64_t ostride = static_cast<int64_t>(p.rows) * D;
 
+  // out is [B / split, Tq, split * Hq, D] (and lse_out likewise without D); with
+  // split 1 the row index is the output row.
+  int64_t orow_idx = row;
+  if (p.request_split != 1) {
+    const int qb = b / p.request_split, part = b - qb * p.request_split;
+    orow_idx = ((static_cast<int64_t>(qb) * p.q_len + t) * p.request_split + part) * p.num_q_heads + h;
+  }
+  uint16_t* orow = p.out + orow_idx * D;
+  if (nb == 1) {  // a single split is already normalised: cast it, pass its lse through
+    if constexpr (E == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(o);
+      *reinterpret_cast<bf16x2*>(orow + 2 * lane) = __builtin_convertvector(v, bf16x2);
+    } else {
+      orow[lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[0]));
+    }
+    if (p.lse_out != nullptr && lane == 0) p.lse_out[orow_idx] = lse[0];
+    return;
+  }
+
   float mloc = -INFINITY;
   for (int i = lane; i < nb; i += 64) mloc = fmaxf(mloc, lse[static_cast<int64_t>(i) * p.rows]);
   const float mx = wave_max(mloc) * kLog2e;  // -inf only if every split saw no key
@@ -98,14 +117,6 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
   }
   den = wave_sum(den);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  // out is [B / split, Tq, split * Hq, D] (and lse_out likewise without D); with
-  // split 1 the row index is the output row.
-  int64_t orow_idx = row;
-  if (p.request_split != 1) {
-    const int qb = b / p.request_split, part = b - qb * p.request_split;
-    orow_idx = ((static_cast<int64_t>(qb) * p.q_len + t) * p.request_split + part) * p.num_q_heads + h;
-  }
-  uint16_t* orow = p.out + orow_idx * D;
   if constexpr (E == 2) {
     f32x2 v = {acc[0] * inv, acc[1] * inv};
     *reinterpret_cast<bf16x2*>(orow + 2 * lane) = __builtin_convertvector(v, bf16x2);

@@ -548,7 +548,8 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
     const int32_t* __restrict__ worker_offsets, const int32_t* __restrict__ tile_dev,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, const DecodeShape sh_arg) {
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, uint16_t* __restrict__ out,
+    float* __restrict__ lse_out, const DecodeShape sh_arg) {
   using C = Cfg<D, FP8, NB>;
   constexpr int kWaves = C::kWaves;
   constexpr int kThreads = C::kThreads;
@@ -720,6 +721,9 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
       process_chunk<D, FP8, NB>(my_stage, qget, acc, rs, j0, lim, c_qk, p_mul, n, gq);
     }
 
+    // A request cut into one tile has its final rows here: with `out` set they are
+    // written there too (work-list requests are the caller's when out is set).
+    const bool direct = out != nullptr && cur.it.tile_start == 0 && cur.it.tile_end == cur.L;
     // Wave result -> LDS: row max and full row sums, then the unnormalised rows of
     // kMergeBlocks column blocks per round, merged across the waves.
 #pragma unroll
@@ -772,6 +776,11 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
           o = num / den;
         }
         wo[e] = o;
+        if (direct) {  // what the combine writes for a single split: bf16(o)
+          const int t = r / G, head = cur.g * G + (r - t * G);
+          out[((static_cast<int64_t>(cur.b) * Tq + t) * sh.num_q_heads + head) * D + d] =
+              __builtin_bit_cast(uint16_t, static_cast<__bf16>(o));
+        }
       }
     }
     for (int r = tid; r < M; r += kThreads) {
@@ -786,6 +795,10 @@ __global__ __launch_bounds__((Cfg<D, FP8, NB>::kThreads), kDecodeGroupsPerCU) vo
         lse = (mx + __builtin_amdgcn_logf(den)) * kLn2;
       }
       ws_lse[static_cast<int64_t>(cur.slot) * M + r] = lse;
+      if (direct && lse_out != nullptr) {  // the combine passes a single split's lse through
+        const int t = r / G, head = cur.g * G + (r - t * G);
+        lse_out[(static_cast<int64_t>(cur.b) * Tq + t) * sh.num_q_heads + head] = lse;
+      }
     }
     __syncthreads();
   }
@@ -802,7 +815,7 @@ void launch_one(const DecodeParams& p, int num_workers, hipStream_t stream) {
   hipLaunchKernelGGL((decode_partial_kernel<D, FP8, NB>), dim3(num_workers),
                      dim3(Cfg<D, FP8, NB>::kThreads), 0, stream, p.q, p.k_cache, p.v_cache,
                      p.k_scale, p.v_scale, p.block_table, p.seq_lens, p.items, p.worker_offsets,
-                     p.tile_tokens_dev, p.ws_o, p.ws_lse, sh);
+                     p.tile_tokens_dev, p.ws_o, p.ws_lse, p.out, p.lse_out, sh);
 }
 
 template <int D, bool FP8>

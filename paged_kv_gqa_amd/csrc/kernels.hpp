@@ -30,6 +30,8 @@ struct DecodeParams {
   int q_len, num_q_heads, num_kv_heads, group, rows, page_size, bt_stride, tile_tokens;
   int request_split;          // work-list request b = part b % split of request b / split
   float qk_scale_log2;        // softmax scale * log2(e)
+  uint16_t* out;              // bf16 [B, Tq, Hq, D] or null: single-tile requests' final rows
+  float* lse_out;             // [B, Tq, Hq] or null
 };
 
 struct CombineParams {

@@ -398,6 +398,42 @@ def test_combine_alone_matches_lse_merge():
                 assert abs(got_lse[b, t, h] - ref_l) <= 1e-5 * max(1.0, abs(ref_l))
 
 
+@pytest.mark.parametrize("fmt,T", [("bf16", 4096), ("bf16", 256), ("fp8", 8192), ("fp8", 128)])
+def test_single_tile_rows_written_by_decode_equal_the_combine(fmt, T):
+    """With out / lse_out in the decode arguments, requests cut into one tile get their
+    final rows from decode_partial itself: bit for bit what the combine writes from the
+    same partials; rows of longer requests are left alone (sentinel kept)."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    from tests.test_zz_no_alloc import step_args
+    inp = medium_inputs(fmt, q_len=2)
+    dev = device_inputs(inp)
+    kw, _plan = step_args(inp, dev, T=T)
+    M = (inp.num_q_heads // inp.num_kv_heads) * inp.q_len
+    nbytes = pkv.pkv_workspace_bytes(max(kw["num_partials"], 1), M, inp.head_dim)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    shape = (inp.batch, inp.q_len, inp.num_q_heads)
+    out_d = torch.full(shape + (inp.head_dim,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse_d = torch.full(shape, 7.0, dtype=torch.float32, device="cuda")
+    pkv.pkv_decode_partial(workspace=ws, workspace_bytes=nbytes, direct_out=out_d, direct_lse_out=lse_d,
+                           **kw)
+    out_c = torch.empty_like(out_d)
+    lse_c = torch.empty_like(lse_d)
+    pkv.pkv_combine(workspace=ws, workspace_bytes=nbytes, num_partials=kw["num_partials"],
+                    req_tile_base=kw["req_tile_base"], batch=inp.batch, q_len=inp.q_len,
+                    num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                    out=out_c, lse_out=lse_c)
+    torch.cuda.synchronize()
+    single = inp.seq_lens <= kw["tile_tokens"]
+    bd = out_d.view(torch.int16).cpu().numpy()
+    bc = out_c.view(torch.int16).cpu().numpy()
+    ld, lc = lse_d.cpu().numpy(), lse_c.cpu().numpy()
+    log("  T=%d: %d of %d requests single-tile" % (kw["tile_tokens"], int(single.sum()), inp.batch))
+    assert single.any()
+    assert np.array_equal(bd[single], bc[single]) and np.array_equal(ld[single], lc[single])
+    assert (out_d.float().cpu().numpy()[~single] == 7.0).all() and (ld[~single] == 7.0).all()
+
+
 def test_empty_batch_is_a_no_op():
     import torch
     inp = synth.make_inputs(cfg(), seed=0, seq_lens=[5])
