@@ -347,6 +347,10 @@ def main():
     ap.add_argument("--event-every", type=int, default=5,
                     help="time the hot kernel with HIP events on every N-th timed step")
     ap.add_argument("--workload", default="mixed")
+    ap.add_argument("--q-len", type=int, default=0,
+                    help="override the workload's query tokens per request (draft tokens)")
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="override the workload's query heads (rows per kv head = q heads / kv heads x q_len)")
     ap.add_argument("--tile-tokens", type=int, default=0)
     ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
@@ -394,7 +398,13 @@ def main():
     import synth
     import paged_kv_gqa_amd as pkv
 
-    cfg = synth.ALL[args.workload]
+    cfg = dict(synth.ALL[args.workload])
+    if args.q_len:
+        cfg["q_len"] = args.q_len
+        cfg["desc"] += "; q_len set to %d" % args.q_len
+    if args.q_heads:
+        cfg["num_q_heads"] = args.q_heads
+        cfg["desc"] += "; q heads set to %d" % args.q_heads
     log("generating %s inputs (seed %d)" % (args.workload, args.seed))
     inp = synth.make_inputs(cfg, seed=args.seed)
     out_bytes = inp.batch * inp.q_len * inp.num_q_heads * inp.head_dim * 2
@@ -492,7 +502,8 @@ def main():
     ms_per_step = wall / K * 1e3
     value = algo / (wall / K) / 1e9
     achieved = partial_algo / kern_avg_s / 1e9
-    traffic = measured_traffic(args.workload) if mask_h is None else None
+    traffic = (measured_traffic(args.workload)
+               if mask_h is None and not (args.q_len or args.q_heads) else None)
     log("%.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s); decode_partial %.1f us avg (%.1f GB/s)" % (
         ms_per_step * 1e3, value, 100 * value / HBM_PEAK_GBS, kern_avg_s * 1e6, achieved))
 
