@@ -67,7 +67,7 @@ def assert_matches_oracle(seq_lens, q_len, Hq, Hkv, D, P, fmt, T, W, cap, tag=""
 
 
 @pytest.mark.parametrize("name", list(synth.ALL))
-@pytest.mark.parametrize("W", [100, 512, 1024])
+@pytest.mark.parametrize("W", [100, 256, 512, 1024])   # 256: the default on MI355X
 def test_workloads_match_oracle(name, W):
     c = synth.ALL[name]
     sl = synth.draw_seq_lens(c, np.random.default_rng(0))
