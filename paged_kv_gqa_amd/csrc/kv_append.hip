@@ -36,42 +36,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Exact value of an e4m3fn code (finite codes; 0x7F / 0xFF give NaN).
+// Exact value of an e4m3fn code (0x7F / 0xFF give NaN). Branch-free: the kernel is
+// short enough that its instruction fetch shows, so the conversions are kept small.
 __device__ __forceinline__ float e4m3fn_value(uint32_t code) {
   const uint32_t sign = (code & 0x80u) << 24;
   const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
-  if (e == 15u && m == 7u) return __uint_as_float(sign | 0x7FC00000u);
-  if (e == 0u) {  // subnormal (and zero): m * 2^-9, exact
-    const float v = static_cast<float>(m) * 0x1p-9f;
-    return sign ? -v : v;
-  }
-  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+  const float normal = __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+  const float sub = __uint_as_float(__float_as_uint(static_cast<float>(m) * 0x1p-9f) | sign);  // m * 2^-9
+  const float nan = __uint_as_float(sign | 0x7FC00000u);
+  return (e == 15u && m == 7u) ? nan : (e == 0u ? sub : normal);
 }
 
 // e4m3fn code of a float32: nearest value, ties to the even code, saturating at 448,
-// sign kept (a negative value that rounds to zero gives 0x80).
+// sign kept (a negative value that rounds to zero gives 0x80). Branch-free:
+// - |x| >= 2^-6: the float32 exponent and top 3 mantissa bits, rounded to nearest
+//   even by adding 2^19 - 1 plus the kept lowest bit below them (a carry moves into the
+//   exponent), rebiased from 127 to 7 and capped at 0x7E (448; 480 and up, and
+//   infinity, would pass it);
+// - |x| < 2^-6: the subnormal codes are the multiples of 2^-9, so the code is
+//   rint(|x| * 512) (exact scaling; rint ties to even; 8 is 2^-6, the first normal);
+// - NaN gives 0x7F.
 __device__ __forceinline__ uint32_t e4m3fn_code(float x) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t sign = (u >> 24) & 0x80u;
   const float ax = fabsf(x);
-  if (ax != ax) return sign | 0x7Fu;
-  if (ax >= 448.f) return sign | 0x7Eu;
-  if (ax < 0x1p-6f) {  // subnormal range: multiples of 2^-9, rounding to 8 gives 2^-6
-    const float q = __builtin_rintf(ax * 512.f);  // exact scaling; rint rounds half to even
-    return sign | static_cast<uint32_t>(q);
-  }
   const uint32_t au = __float_as_uint(ax);
-  uint32_t e = ((au >> 23) & 0xFFu) - 127u + 7u;  // e4m3fn biased exponent, 1 .. 15
-  uint32_t m = (au >> 20) & 7u;
-  const uint32_t rest = au & 0xFFFFFu, half = 0x80000u;
-  if (rest > half || (rest == half && (m & 1u))) {
-    if (++m == 8u) {
-      m = 0;
-      ++e;
-    }
-  }
-  const uint32_t code = (e << 3) | m;
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
+  const uint32_t normal = min(((au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20) - (120u << 3), 0x7Eu);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(fminf(ax, 0x1p-6f) * 512.f));  // 0 .. 8
+  uint32_t code = ax < 0x1p-6f ? sub : normal;
+  code = (ax != ax) ? 0x7Fu : code;
+  return sign | code;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -81,6 +75,7 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Four consecutive bf16 values (8 bytes) -> float32.
 __device__ __forceinline__ void load4(const uint16_t* src, float (&x)[4]) {
@@ -96,32 +91,43 @@ __device__ __forceinline__ u32x2 pack4_bf16(const float (&x)[4]) {
                static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16)};
 }
 
+// Four consecutive table values (the tables need only 4-byte alignment: element loads).
+__device__ __forceinline__ void load_row4(const float* src, float (&x)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = src[j];
+}
+
 // Rotation of one lane's four pairs (x1[j], x2[j]) = (x[i0 + j], x[i0 + j + D/2]) of a
-// row at position pos.
-// (The tables need only 4-byte alignment: element loads.)
-__device__ __forceinline__ void rotate4(float (&x1)[4], float (&x2)[4], const float* cos_row,
-                                        const float* sin_row) {
+// row by the table values (c[j], s[j]) of its position.
+__device__ __forceinline__ void rotate4(float (&x1)[4], float (&x2)[4], const float (&c)[4],
+                                        const float (&s)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float c = cos_row[j], s = sin_row[j];
-    const float r1 = x1[j] * c - x2[j] * s;
-    const float r2 = x2[j] * c + x1[j] * s;
+    const float r1 = x1[j] * c[j] - x2[j] * s[j];
+    const float r2 = x2[j] * c[j] + x1[j] * s[j];
     x1[j] = r1;
     x2[j] = r2;
   }
 }
 
+// Query-row quads a thread rotates with their loads issued up front (the rest, with
+// more query heads or draft tokens, in a loop afterwards).
+constexpr int kQPre = 2;
+
 // One workgroup of four waves per (request b, kv head g). Wave 2p + kind writes the
 // new rows of touched page p (0: the page of the first new token, 1: the next one,
 // if touched) of K (kind 0, rotated) or V (kind 1); each lane holds four rotation
 // pairs (i0 .. i0+3 and the same + D/2 of one row), so the page's largest |value|
-// is a wave reduction and no step waits for another wave. The page's old scale is
-// loaded first, beside the rows. For FP8, one barrier then lets the whole workgroup
-// re-encode page 0's earlier rows if its scale rose. Then every thread rotates the
-// new q rows of the kv head's query heads.
+// is a wave reduction and no step waits for another wave. Every thread also rotates
+// four pairs of the new q rows of the kv head's query heads. All loads that need only
+// the request's length (block-table entry, new k/v rows, q rows, rotation tables) are
+// issued together, then the page scale (which needs the block-table entry); so the
+// kernel waits for memory about twice before its stores. For FP8, one barrier then
+// lets the whole workgroup re-encode page 0's earlier rows if its scale rose.
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParams p) {
   __shared__ int re_flag[2];          // page 0 of K / V needs its earlier rows re-encoded
   __shared__ float re_scale[2][2];    // (old, new) scale of page 0 of K / V
+  __shared__ int64_t re_phys;         // physical page of page 0
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -132,37 +138,89 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
   const int first = L - Tq;
   const bool rope = p.rope_cos != nullptr;
 
+  // This wave's page and rows.
   const int lp = first / P + (wid >> 1);
   const int kind = wid & 1;
-  if (lp <= (L - 1) / P) {  // this wave's page is touched (wave-uniform)
-    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-    const int64_t phys = bt[lp];
-    const int o0 = max(first, lp * P) - lp * P;
-    const int o1 = min(L, (lp + 1) * P) - lp * P;
-    const int n = o1 - o0;                     // new rows in this page, 1 .. Tq
-    const int t0 = lp * P + o0 - first;        // their first new-token index
-    const int64_t sidx = phys * p.num_kv_heads + g;
-    float* scales = kind == 0 ? p.k_scale : p.v_scale;
-    const float s_old = p.fp8 ? scales[sidx] : 1.f;
-    const uint16_t* src = kind == 0 ? p.k_new : p.v_new;
-    uint8_t* cache = kind == 0 ? p.k_cache : p.v_cache;
-    const int64_t slot = sidx * P;             // row 0 of the page's kv-head run
-
-    const int e0 = 4 * lane;                   // first of this lane's four pairs
-    const bool act = e0 < n * H;
-    const int r = act ? e0 / H : 0, i0 = act ? e0 - r * H : 0;
-    float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool touched = lp <= (L - 1) / P;  // wave-uniform
+  const int o0 = max(first, lp * P) - lp * P;
+  const int o1 = min(L, (lp + 1) * P) - lp * P;
+  const int n = o1 - o0;                   // new rows in this page, 1 .. Tq (if touched)
+  const int t0 = lp * P + o0 - first;      // their first new-token index
+  const int e0 = 4 * lane;                 // first of this lane's four pairs
+  const bool act = touched && e0 < n * H;
+  const int r = act ? e0 / H : 0, i0 = act ? e0 - r * H : 0;
+  int64_t phys = 0;
+  float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
+  float kc[4], ks[4];
+  const bool rot_k = rope && kind == 0;
+  if (touched) {
+    phys = p.block_table[static_cast<int64_t>(b) * p.bt_stride + lp];
     if (act) {
-      const int t = t0 + r;
-      const int64_t in = ((static_cast<int64_t>(b) * Tq + t) * p.num_kv_heads + g) * D;
+      const uint16_t* src = kind == 0 ? p.k_new : p.v_new;
+      const int64_t in = ((static_cast<int64_t>(b) * Tq + t0 + r) * p.num_kv_heads + g) * D;
       load4(src + in + i0, x1);
       load4(src + in + i0 + H, x2);
-      if (rope && kind == 0) {
-        const int64_t pos = first + t;
-        rotate4(x1, x2, p.rope_cos + pos * H + i0, p.rope_sin + pos * H + i0);
+      if (rot_k) {
+        const int64_t pos = first + t0 + r;
+        load_row4(p.rope_cos + pos * H + i0, kc);
+        load_row4(p.rope_sin + pos * H + i0, ks);
       }
     }
-    const int64_t row = slot + o0 + r;
+  }
+
+  // The first q quads of this thread: rows of query heads g*G .. g*G+G-1.
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int qn = (rope && p.q_out != nullptr) ? Tq * G * H : 0;
+  float qx1[kQPre][4], qx2[kQPre][4], qc[kQPre][4], qs[kQPre][4];
+  int64_t qrow[kQPre];
+  int qi0[kQPre];
+#pragma unroll
+  for (int k = 0; k < kQPre; ++k) {
+    const int e = 4 * tid + 4 * kThreads * k;
+    qrow[k] = -1;
+    if (e < qn) {
+      const int t = e / (G * H), j = (e / H) % G;
+      qi0[k] = e % H;
+      const int64_t pos = first + t;
+      qrow[k] = ((static_cast<int64_t>(b) * Tq + t) * p.num_q_heads + g * G + j) * D;
+      load4(p.q + qrow[k] + qi0[k], qx1[k]);
+      load4(p.q + qrow[k] + qi0[k] + H, qx2[k]);
+      load_row4(p.rope_cos + pos * H + qi0[k], qc[k]);
+      load_row4(p.rope_sin + pos * H + qi0[k], qs[k]);
+    }
+  }
+
+  // The page scale (FP8): the one load that waits for the block-table entry.
+  const int64_t sidx = phys * p.num_kv_heads + g;
+  float* scales = kind == 0 ? p.k_scale : p.v_scale;
+  const float s_old = (p.fp8 && touched) ? scales[sidx] : 1.f;
+
+#pragma unroll
+  for (int k = 0; k < kQPre; ++k) {
+    if (qrow[k] >= 0) {
+      rotate4(qx1[k], qx2[k], qc[k], qs[k]);
+      *reinterpret_cast<u32x2*>(p.q_out + qrow[k] + qi0[k]) = pack4_bf16(qx1[k]);
+      *reinterpret_cast<u32x2*>(p.q_out + qrow[k] + qi0[k] + H) = pack4_bf16(qx2[k]);
+    }
+  }
+  for (int e = 4 * tid + 4 * kThreads * kQPre; e < qn; e += 4 * kThreads) {
+    const int t = e / (G * H), j = (e / H) % G, qi = e % H;
+    const int64_t pos = first + t;
+    const int64_t row = ((static_cast<int64_t>(b) * Tq + t) * p.num_q_heads + g * G + j) * D;
+    float y1[4], y2[4], c[4], sn[4];
+    load4(p.q + row + qi, y1);
+    load4(p.q + row + qi + H, y2);
+    load_row4(p.rope_cos + pos * H + qi, c);
+    load_row4(p.rope_sin + pos * H + qi, sn);
+    rotate4(y1, y2, c, sn);
+    *reinterpret_cast<u32x2*>(p.q_out + row + qi) = pack4_bf16(y1);
+    *reinterpret_cast<u32x2*>(p.q_out + row + qi + H) = pack4_bf16(y2);
+  }
+
+  if (touched) {
+    uint8_t* cache = kind == 0 ? p.k_cache : p.v_cache;
+    const int64_t row = sidx * P + o0 + r;  // row o0 + r of the page's kv-head run
+    if (act && rot_k) rotate4(x1, x2, kc, ks);
     if (!p.fp8) {
       if (act) {
         uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + row * D;
@@ -182,13 +240,19 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
         s = s_old;
         if (!(a / s <= 448.f)) {
           s = a / 448.f;
-          again = true;
+          // A "raised" scale equal to the old one (a / s rounds just above 448 while
+          // a / 448 rounds back to s) would re-encode every earlier code to itself: the
+          // round trip code value * s / s moves a value by at most 2^-23 relative, far
+          // below half an e4m3fn step, while s lies in [2^-100, 2^118] (no float32
+          // underflow or overflow on the way). So that re-encode is skipped.
+          again = !(s == s_old && s_old >= 0x1p-100f && s_old <= 0x1p118f);
         }
       }
       if (wid < 2 && lane == 0) {  // page 0: whether its earlier rows need re-encoding
         re_flag[kind] = again ? 1 : 0;
         re_scale[kind][0] = s_old;
         re_scale[kind][1] = s;
+        if (kind == 0) re_phys = phys;
       }
       if (act) {
         uint32_t c1 = 0, c2 = 0;
@@ -205,45 +269,52 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
   }
 
   // A raised scale of page 0 re-encodes that page's earlier rows (o < o0) from their
-  // values under the old scale; the whole workgroup shares the work. Those rows are
-  // disjoint from the new ones written above.
+  // values under the old scale; the whole workgroup shares the work, each thread
+  // loading all of its 16-byte units before converting any (one wait for memory).
+  // Those rows are disjoint from the new ones written above.
   if (p.fp8) {
     __syncthreads();
-    const int lp0 = first / P;
-    const int o0 = first - lp0 * P;
+    const int nflag = re_flag[0] + re_flag[1];
+    if (nflag != 0) {
+      const int o0p = first - (first / P) * P;
+      const int units = o0p * D / 16;  // 16-byte units of the earlier rows of one page
+      const int kfirst = re_flag[0] ? 0 : 1;
+      const int64_t run = (re_phys * p.num_kv_heads + g) * P * D;
+      const int total = nflag * units;  // units of the flagged kinds, kfirst's first
+      constexpr int kBatch = 4;
+      for (int f0 = 0; f0 < total; f0 += kBatch * kThreads) {
+        u32x4 w[kBatch];
 #pragma unroll
-    for (int kind = 0; kind < 2; ++kind) {
-      if (re_flag[kind]) {
-        const int64_t phys = p.block_table[static_cast<int64_t>(b) * p.bt_stride + lp0];
-        uint8_t* page = (kind == 0 ? p.k_cache : p.v_cache) + (phys * p.num_kv_heads + g) * P * D;
-        const float s_old = re_scale[kind][0], s = re_scale[kind][1];
-        for (int e = 4 * tid; e < o0 * D; e += 4 * kThreads) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(page + e);
-          uint32_t out = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float v = e4m3fn_value((w >> (8 * j)) & 0xFFu) * s_old;
-            out |= e4m3fn_code(v / s) << (8 * j);
+        for (int j = 0; j < kBatch; ++j) {
+          const int f = f0 + j * kThreads + tid;
+          if (f < total) {
+            const int kd = f < units ? kfirst : 1;
+            const uint8_t* page = (kd == 0 ? p.k_cache : p.v_cache) + run;
+            w[j] = *reinterpret_cast<const u32x4*>(page + 16 * static_cast<int64_t>(f < units ? f : f - units));
           }
-          *reinterpret_cast<uint32_t*>(page + e) = out;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int f = f0 + j * kThreads + tid;
+          if (f < total) {
+            const int kd = f < units ? kfirst : 1;
+            uint8_t* page = (kd == 0 ? p.k_cache : p.v_cache) + run;
+            const float so = re_scale[kd][0], sn = re_scale[kd][1];
+            uint32_t* dst = reinterpret_cast<uint32_t*>(page + 16 * static_cast<int64_t>(f < units ? f : f - units));
+#pragma unroll 1
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t word = i == 0 ? w[j].x : i == 1 ? w[j].y : i == 2 ? w[j].z : w[j].w;
+              uint32_t o = 0;
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const float v = e4m3fn_value((word >> (8 * jj)) & 0xFFu) * so;
+                o |= e4m3fn_code(v / sn) << (8 * jj);
+              }
+              dst[i] = o;
+            }
+          }
         }
       }
-    }
-  }
-
-  // Rotation of the new q rows of this kv head's query heads: four pairs per thread.
-  if (rope && p.q_out != nullptr) {
-    const int G = p.num_q_heads / p.num_kv_heads;
-    for (int e = 4 * tid; e < Tq * G * H; e += 4 * kThreads) {
-      const int t = e / (G * H), j = (e / H) % G, i0 = e % H;
-      const int64_t pos = first + t;
-      const int64_t qrow = ((static_cast<int64_t>(b) * Tq + t) * p.num_q_heads + g * G + j) * D;
-      float x1[4], x2[4];
-      load4(p.q + qrow + i0, x1);
-      load4(p.q + qrow + i0 + H, x2);
-      rotate4(x1, x2, p.rope_cos + pos * H + i0, p.rope_sin + pos * H + i0);
-      *reinterpret_cast<u32x2*>(p.q_out + qrow + i0) = pack4_bf16(x1);
-      *reinterpret_cast<u32x2*>(p.q_out + qrow + i0 + H) = pack4_bf16(x2);
     }
   }
 }

@@ -299,3 +299,41 @@ def test_graph_captured_step_with_append():
         log("  token %d: replay equals the eager step" % step)
     for name in ("k", "v"):
         assert torch.equal(dev_g[name].view(torch.int16), dev_e[name].view(torch.int16)), name
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_reappending_the_same_rows_matches_oracle(P):
+    """The same new rows appended again at the same positions (as a benchmark loop does):
+    where fl(a / s) lands just above 448 while fl(a / 448) == s, the rule raises the scale
+    to its own value and re-encodes every earlier code to itself; the kernel skips that
+    no-op and must still equal the oracle bit for bit, on every repeat."""
+    import torch
+    c = cfg(kv_format="fp8", page_size=P, q_len=4, num_q_heads=16, num_kv_heads=4)
+    lens = [5, 6, 7, 30, 61, 62, 63, 100, 127, 200, 301, 777]
+    inp = synth.make_inputs(c, seed=51, slack_pages=2, seq_lens=lens)
+    k_new, v_new, q = synth.new_token_rows(inp, seed=52, scale=3.0)   # beyond the pages: scales rise
+    dev = device_inputs(inp)
+    equal_raises = 0
+    for rep in range(4):
+        dev["sl"].copy_(torch.from_numpy(inp.seq_lens))
+        if rep > 0:  # count the pages whose scale the rule raises to the same value
+            for b, L in enumerate(inp.seq_lens):
+                first = int(L) - inp.q_len
+                lp = first // P
+                o0 = first - lp * P
+                if o0 == 0:
+                    continue
+                phys = int(inp.block_table[b, lp])
+                n = min(int(L), (lp + 1) * P) - first
+                for g in range(inp.num_kv_heads):
+                    for rows, sc in ((k_new, inp.k_scale), (v_new, inp.v_scale)):
+                        vals = (rows[b, :n, g].astype(np.uint32) << 16).view(np.float32)
+                        a = np.float32(np.max(np.abs(vals)))
+                        s = np.float32(sc[phys, g])
+                        if not (np.float32(a / s) <= np.float32(448.0)) and np.float32(a / np.float32(448.0)) == s:
+                            equal_raises += 1
+        gpu_append(inp, dev, k_new, v_new, None, None)
+        oracle_append(inp, k_new, v_new, None, None)
+        assert_same(inp, dev, None, None, "repeat %d" % rep)
+    log("  P=%d: %d equal-scale raises over the repeats" % (P, equal_raises))
+    assert equal_raises > 0
