@@ -38,9 +38,11 @@ namespace pkv {
 namespace {
 
 // Threads of a planner workgroup: one per worker (and per request for the register
-// sort of the request keys), so 512 when W and B allow it, else 1024.
+// sort of the request keys), so 256 or 512 when W and B allow it, else 1024 (fewer
+// waves meet at each of the plan's barriers).
 constexpr int kPT = 1024;
 constexpr int kPTSmall = 512;
+constexpr int kPTTiny = 256;
 constexpr int kWorkerBits = 10;           // worker index in the low bits of a key
 constexpr int kReqBits = 13;              // request index in the low bits of a key
 constexpr long long kMaxTokenHeads = 1LL << 36;
@@ -51,7 +53,8 @@ typedef unsigned u32;
 
 static_assert(kMaxDevicePlanWorkers <= kPT && kMaxDevicePlanWorkers <= (1 << kWorkerBits),
               "one thread and one key field per worker");
-static_assert(kPTSmall % 64 == 0 && kPTSmall <= kPT, "planner workgroup sizes");
+static_assert(kPTSmall % 64 == 0 && kPTSmall <= kPT && kPTTiny % 64 == 0 && kPTTiny <= kPTSmall,
+              "planner workgroup sizes");
 static_assert(kMaxDevicePlanBatch <= (1 << kReqBits), "request index field");
 // Remainder-tile key (T - c) << kReqBits | b and worker key (relative load < 2T) <<
 // kWorkerBits | w stay below 2^31, so ~0u is a sentinel above every key.
@@ -576,9 +579,13 @@ __global__ __launch_bounds__(NT) void plan_fixed_kernel(const DevicePlanParams p
 }  // namespace
 
 hipError_t launch_plan_device(const DevicePlanParams& p, hipStream_t stream) {
+  const bool tiny = p.num_workers <= kPTTiny && p.batch <= kPTTiny;
   const bool small = p.num_workers <= kPTSmall && p.batch <= kPTSmall;
   if (p.tile_tokens == 0) {
-    if (small)
+    if (tiny)
+      hipLaunchKernelGGL(plan_candidates_kernel<kPTTiny>, dim3(p.num_candidates), dim3(kPTTiny), 0,
+                         stream, p);
+    else if (small)
       hipLaunchKernelGGL(plan_candidates_kernel<kPTSmall>, dim3(p.num_candidates), dim3(kPTSmall), 0,
                          stream, p);
     else
@@ -587,7 +594,9 @@ hipError_t launch_plan_device(const DevicePlanParams& p, hipStream_t stream) {
     const int grid = static_cast<int>(blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks));
     hipLaunchKernelGGL(plan_select_kernel, dim3(grid), dim3(kPT), 0, stream, p);
   } else {
-    if (small)
+    if (tiny)
+      hipLaunchKernelGGL(plan_fixed_kernel<kPTTiny>, dim3(1), dim3(kPTTiny), 0, stream, p);
+    else if (small)
       hipLaunchKernelGGL(plan_fixed_kernel<kPTSmall>, dim3(1), dim3(kPTSmall), 0, stream, p);
     else
       hipLaunchKernelGGL(plan_fixed_kernel<kPT>, dim3(1), dim3(kPT), 0, stream, p);
