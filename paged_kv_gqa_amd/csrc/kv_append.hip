@@ -25,7 +25,8 @@
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 256;  // four waves: (page 0, 1) x (K, V)
+// Waves per workgroup: (page 0, 1) x (K, V); one new token per request touches one
+// page, so two waves (page 0's K and V) do then.
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -91,7 +92,8 @@ __device__ __forceinline__ u32x2 pack4_bf16(const float (&x)[4]) {
                static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16)};
 }
 
-// Four consecutive table values (the tables need only 4-byte alignment: element loads).
+// Four consecutive table values (the tables need only 4-byte alignment: element loads;
+// 16-byte loads where the tables allow them measured no faster).
 __device__ __forceinline__ void load_row4(const float* src, float (&x)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) x[j] = src[j];
@@ -124,7 +126,9 @@ constexpr int kQPre = 2;
 // issued together, then the page scale (which needs the block-table entry); so the
 // kernel waits for memory about twice before its stores. For FP8, one barrier then
 // lets the whole workgroup re-encode page 0's earlier rows if its scale rose.
-__global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParams p) {
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void kv_append_kernel(const KvAppendParams p) {
+  constexpr int kThreads = 64 * kWaves;
   __shared__ int re_flag[2];          // page 0 of K / V needs its earlier rows re-encoded
   __shared__ float re_scale[2][2];    // (old, new) scale of page 0 of K / V
   __shared__ int64_t re_phys;         // physical page of page 0
@@ -174,9 +178,12 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
   float qx1[kQPre][4], qx2[kQPre][4], qc[kQPre][4], qs[kQPre][4];
   int64_t qrow[kQPre];
   int qi0[kQPre];
+  // Thread order for the q quads starts at the second wave, so that with one new token
+  // (two waves) the V wave rotates q while the K wave rotates k.
+  const int qtid = (tid + 64) % kThreads;
 #pragma unroll
   for (int k = 0; k < kQPre; ++k) {
-    const int e = 4 * tid + 4 * kThreads * k;
+    const int e = 4 * qtid + 4 * kThreads * k;
     qrow[k] = -1;
     if (e < qn) {
       const int t = e / (G * H), j = (e / H) % G;
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
       *reinterpret_cast<u32x2*>(p.q_out + qrow[k] + qi0[k] + H) = pack4_bf16(qx2[k]);
     }
   }
-  for (int e = 4 * tid + 4 * kThreads * kQPre; e < qn; e += 4 * kThreads) {
+  for (int e = 4 * qtid + 4 * kThreads * kQPre; e < qn; e += 4 * kThreads) {
     const int t = e / (G * H), j = (e / H) % G, qi = e % H;
     const int64_t pos = first + t;
     const int64_t row = ((static_cast<int64_t>(b) * Tq + t) * p.num_q_heads + g * G + j) * D;
@@ -322,7 +329,10 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendParam
 }  // namespace
 
 hipError_t launch_kv_append(const KvAppendParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(kv_append_kernel, dim3(p.batch * p.num_kv_heads), dim3(kThreads), 0, stream, p);
+  if (p.q_len == 1)
+    hipLaunchKernelGGL(kv_append_kernel<2>, dim3(p.batch * p.num_kv_heads), dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<4>, dim3(p.batch * p.num_kv_heads), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -337,3 +337,35 @@ def test_reappending_the_same_rows_matches_oracle(P):
         assert_same(inp, dev, None, None, "repeat %d" % rep)
     log("  P=%d: %d equal-scale raises over the repeats" % (P, equal_raises))
     assert equal_raises > 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_rope_tables_with_4_byte_alignment(fmt):
+    """Rotation tables that are 4-byte but not 16-byte aligned (the contract's minimum):
+    the kernel reads them element by element and must match the oracle bit for bit."""
+    import torch
+    import paged_kv_gqa_amd as pkv
+    c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2, num_q_heads=8, num_kv_heads=2)
+    inp = synth.make_inputs(c, seed=61, slack_pages=2, seq_lens=[2, 17, 64, 65, 300])
+    k_new, v_new, q = synth.new_token_rows(inp, seed=62, scale=2.0)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim)
+    dev = device_inputs(inp)
+    t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    tabs = []
+    for x in rope:
+        flat = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+        flat[1:] = torch.from_numpy(x.reshape(-1)).cuda()
+        tab = flat[1:].view(x.shape)
+        assert tab.data_ptr() % 16 == 4
+        tabs.append(tab)
+    qd = t(q)
+    q_out = torch.empty_like(qd)
+    pkv.pkv_kv_append(k_new=t(k_new), v_new=t(v_new), k_cache=dev["k"], v_cache=dev["v"], block_table=dev["bt"],
+                      seq_lens=dev["sl"], num_pages=dev["k"].shape[0], batch=inp.batch, q_len=inp.q_len,
+                      num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                      page_size=inp.page_size, bt_stride=inp.block_table.shape[1], kv_format=inp.kv_format,
+                      q=qd, q_out=q_out, rope_cos=tabs[0], rope_sin=tabs[1], max_pos=rope[0].shape[0],
+                      k_scale=dev["ks"], v_scale=dev["vs"])
+    torch.cuda.synchronize()
+    q_ref = oracle_append(inp, k_new, v_new, q, rope)
+    assert_same(inp, dev, q_out.view(torch.int16).cpu().numpy().view(np.uint16), q_ref, "unaligned tables")
