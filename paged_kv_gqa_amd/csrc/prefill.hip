@@ -461,16 +461,22 @@ void prefill_kernel(const PrefillParams p) {
   // FP8 page scales of the block being computed, one per 16-key half (a half lies in
   // one page; the two may differ when pages are shorter than 32 keys or not aligned to
   // blocks), and the physical pages of the next block's halves.
+  // With pages a multiple of 32 keys a block lies in one page: its second half takes
+  // the first half's scales, with no second lookup.
   float ksc[2] = {1.f, 1.f}, vsc[2] = {1.f, 1.f};
   int scale_page[2] = {0, 0};
   auto half_page = [&](int j) { return bt[min(j, L - 1) / p.page_size]; };
+  const int scale_halves = (p.page_size % kBlockKeys == 0) ? 1 : 2;
   if constexpr (FP8) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < scale_halves; ++h) {
       const int64_t sidx = static_cast<int64_t>(half_page(16 * h)) * p.num_kv_heads + g;
       ksc[h] = p.k_scale[sidx];
       vsc[h] = p.v_scale[sidx];
       scale_page[h] = half_page(kBlockKeys + 16 * h);
+    }
+    if (scale_halves == 1) {
+      ksc[1] = ksc[0];
+      vsc[1] = vsc[0];
     }
   }
   for (int kb = 0; kb < nblocks; ++kb) {
@@ -482,12 +488,15 @@ void prefill_kernel(const PrefillParams p) {
       load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, kb + 1, L, tid);
       if (kb + 2 < nblocks) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
       if constexpr (FP8) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < scale_halves; ++h) {
           const int64_t sidx = static_cast<int64_t>(scale_page[h]) * p.num_kv_heads + g;
           ksc_next[h] = p.k_scale[sidx];
           vsc_next[h] = p.v_scale[sidx];
           if (kb + 2 < nblocks) scale_page[h] = half_page((kb + 2) * kBlockKeys + 16 * h);
+        }
+        if (scale_halves == 1) {
+          ksc_next[1] = ksc_next[0];
+          vsc_next[1] = vsc_next[0];
         }
       }
     }
