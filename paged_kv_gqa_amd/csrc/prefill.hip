@@ -463,16 +463,30 @@ void prefill_kernel(const PrefillParams p) {
   // blocks), and the physical pages of the next block's halves.
   // With pages a multiple of 32 keys a block lies in one page: its second half takes
   // the first half's scales, with no second lookup.
+  // The logical page (and row in it) of each half's first key is advanced by one block
+  // per step, so no division by the page size per block; pages past the last clamp to
+  // it (keys past the length are masked).
   float ksc[2] = {1.f, 1.f}, vsc[2] = {1.f, 1.f};
   int scale_page[2] = {0, 0};
-  auto half_page = [&](int j) { return bt[min(j, L - 1) / p.page_size]; };
+  int hpg[2] = {0, 0}, hrow[2] = {0, 0};  // logical page and row of half h's first key
+  auto half_phys = [&](int h) { return bt[min(hpg[h], last_page)]; };
+  auto half_advance = [&](int h) {  // by one block of keys
+    hrow[h] += kBlockKeys;
+    while (hrow[h] >= p.page_size) {
+      hrow[h] -= p.page_size;
+      ++hpg[h];
+    }
+  };
   const int scale_halves = (p.page_size % kBlockKeys == 0) ? 1 : 2;
   if constexpr (FP8) {
     for (int h = 0; h < scale_halves; ++h) {
-      const int64_t sidx = static_cast<int64_t>(half_page(16 * h)) * p.num_kv_heads + g;
+      hpg[h] = (16 * h) / p.page_size;
+      hrow[h] = 16 * h - hpg[h] * p.page_size;
+      const int64_t sidx = static_cast<int64_t>(half_phys(h)) * p.num_kv_heads + g;
       ksc[h] = p.k_scale[sidx];
       vsc[h] = p.v_scale[sidx];
-      scale_page[h] = half_page(kBlockKeys + 16 * h);
+      half_advance(h);
+      scale_page[h] = half_phys(h);
     }
     if (scale_halves == 1) {
       ksc[1] = ksc[0];
@@ -492,7 +506,10 @@ void prefill_kernel(const PrefillParams p) {
           const int64_t sidx = static_cast<int64_t>(scale_page[h]) * p.num_kv_heads + g;
           ksc_next[h] = p.k_scale[sidx];
           vsc_next[h] = p.v_scale[sidx];
-          if (kb + 2 < nblocks) scale_page[h] = half_page((kb + 2) * kBlockKeys + 16 * h);
+          if (kb + 2 < nblocks) {
+            half_advance(h);
+            scale_page[h] = half_phys(h);
+          }
         }
         if (scale_halves == 1) {
           ksc_next[1] = ksc_next[0];
