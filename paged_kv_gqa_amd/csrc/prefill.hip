@@ -30,12 +30,14 @@
 //   4k..4k+3 address row k of a 4 x 16 tile of 16-bit values and lane i receives
 //   column i) gives lane (n, gq) the four keys 4gq + 0..3 (then 16 + 4gq + 0..3) of
 //   head dim 16bl + n, i.e. V^T's A operand, in two reads.
-// - The next block's K and V are loaded into registers while the current one is
-//   computed (double-buffered stage, one barrier per block); the block-table entries
-//   are fetched one block earlier still.
-// FP8 (e4m3fn) K/V bytes are widened to bf16 exactly when staged, once per workgroup;
-// each 16-key half of a block lies in one page, whose K scale multiplies that half's
-// scores and whose V scale its P.
+// - Blocks are software-pipelined: while block kb's exponentials run, the wave reads
+//   block kb + 1's K operands and issues its score products, so matrix, vector and LDS
+//   work overlap inside one wave. The stage is triple-buffered with one barrier per
+//   block; the K/V loads for the stage run one block ahead, the block-table entries
+//   one block earlier still.
+// FP8 (e4m3fn) K/V bytes are widened to bf16 exactly when staged, once per workgroup
+// and spread over all of its threads; each 16-key half of a block lies in one page,
+// whose K scale multiplies that half's scores and whose V scale its P.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -109,8 +111,6 @@ template <int D, bool FP8>
 struct PCfg {
   static constexpr int kEb = FP8 ? 1 : 2;
   static constexpr int kRowBytes = D * kEb;               // one K or V row in the cache
-  static constexpr int kRowUnits = kRowBytes / 16;        // 16-byte units per cache row
-  static constexpr int kBlockUnits = kBlockKeys * kRowUnits;
   static constexpr int kSteps = D / 32;                   // MFMA k-steps over D
   static constexpr int kDimBlocks = D / 16;               // 16-dim blocks of O^T
 };
@@ -130,25 +130,43 @@ struct Stage {
   alignas(16) uint8_t v[kBlockKeys * kVStride];
 };
 
-// 16-byte cache units of one block per thread (fp8 with 512 threads: half the
-// threads stage nothing), with each unit's page walk: the physical page and in-page
-// row of the next block to load, and the logical page and in-page row of the block
-// after it (advanced by 32 keys per block, so no division by the page size).
+// A block's K (and V) bytes split into equal units, one per thread where the
+// workgroup has enough threads: 16-byte units for bf16; for fp8, whose block holds half
+// the bytes, units of 8 (or 4) bytes when 16-byte units would leave threads idle, so
+// that every wave shares the widening to bf16.
+template <int D, bool FP8, int NT>
+struct Units {
+  static constexpr int kRowBytes = PCfg<D, FP8>::kRowBytes;
+  static constexpr int kFit = kBlockKeys * kRowBytes / NT;  // bytes per thread
+  static constexpr int kBytes = !FP8 || kFit >= 16 ? 16 : (kFit >= 8 ? 8 : 4);
+  static constexpr int kWords = kBytes / 4;
+  static constexpr int kRowUnits = kRowBytes / kBytes;     // units per cache row
+  static constexpr int kBlockUnits = kBlockKeys * kRowUnits;
+  static constexpr int kPerThread = (kBlockUnits + NT - 1) / NT;
+};
+
+template <int N>
+using uvec = unsigned __attribute__((ext_vector_type(N)));
+
+// This thread's units of one block, with each unit's page walk: the physical page and
+// in-page row of the next block to load, and the logical page and in-page row of the
+// block after it (advanced by 32 keys per block, so no division by the page size).
 template <int D, bool FP8, int NT>
 struct BlockRegs {
-  static constexpr int kUnits = (PCfg<D, FP8>::kBlockUnits + NT - 1) / NT;
-  u32x4 k[kUnits];
-  u32x4 v[kUnits];
+  using U = Units<D, FP8, NT>;
+  static constexpr int kUnits = U::kPerThread;
+  uvec<U::kWords> k[kUnits];
+  uvec<U::kWords> v[kUnits];
   int phys[kUnits], load_off[kUnits];
   int walk_page[kUnits], walk_off[kUnits];
 };
 
 template <int D, bool FP8, int NT>
 __device__ __forceinline__ void walk_init(BlockRegs<D, FP8, NT>& r, int page_size, int tid) {
-  using C = PCfg<D, FP8>;
+  using U = Units<D, FP8, NT>;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
-    const int row = (tid + NT * i) / C::kRowUnits;  // < 32 for staging units
+  for (int i = 0; i < U::kPerThread; ++i) {
+    const int row = (tid + NT * i) / U::kRowUnits;  // < 32 for staging units
     r.walk_page[i] = row / page_size;
     r.walk_off[i] = row % page_size;
   }
@@ -159,10 +177,10 @@ __device__ __forceinline__ void walk_init(BlockRegs<D, FP8, NT>& r, int page_siz
 template <int D, bool FP8, int NT>
 __device__ __forceinline__ void block_pages(BlockRegs<D, FP8, NT>& r, const int32_t* __restrict__ bt,
                                             int last_page, int page_size, int tid) {
-  using C = PCfg<D, FP8>;
+  using U = Units<D, FP8, NT>;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
-    const bool staged = tid + NT * i < C::kBlockUnits;
+  for (int i = 0; i < U::kPerThread; ++i) {
+    const bool staged = tid + NT * i < U::kBlockUnits;
     r.phys[i] = staged ? bt[min(r.walk_page[i], last_page)] : 0;
     r.load_off[i] = r.walk_off[i];
     int off = r.walk_off[i] + kBlockKeys, page = r.walk_page[i];
@@ -180,19 +198,20 @@ template <int D, bool FP8, int NT>
 __device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const uint8_t* __restrict__ kc,
                                            const uint8_t* __restrict__ vc, int64_t page_bytes,
                                            int64_t head_off, int kb, int L, int tid) {
-  using C = PCfg<D, FP8>;
+  using U = Units<D, FP8, NT>;
+  using V = uvec<U::kWords>;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
+  for (int i = 0; i < U::kPerThread; ++i) {
     const int u = tid + NT * i;
-    const int row = u / C::kRowUnits, unit = u % C::kRowUnits;
-    if (u < C::kBlockUnits && kb * kBlockKeys + row < L) {
+    const int row = u / U::kRowUnits, unit = u % U::kRowUnits;
+    if (u < U::kBlockUnits && kb * kBlockKeys + row < L) {
       const int64_t off = static_cast<int64_t>(r.phys[i]) * page_bytes + head_off +
-                          r.load_off[i] * C::kRowBytes + 16 * unit;
-      r.k[i] = *reinterpret_cast<const u32x4*>(kc + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vc + off);
+                          r.load_off[i] * U::kRowBytes + U::kBytes * unit;
+      r.k[i] = *reinterpret_cast<const V*>(kc + off);
+      r.v[i] = *reinterpret_cast<const V*>(vc + off);
     } else {
-      r.k[i] = u32x4{0u, 0u, 0u, 0u};
-      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      r.k[i] = V{};
+      r.v[i] = V{};
     }
   }
 }
@@ -200,23 +219,27 @@ __device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const uint8
 // K and V rows into LDS as bf16 (fp8 widened exactly), row-major.
 template <int D, bool FP8, int NT>
 __device__ __forceinline__ void stage_block(Stage<D>& st, const BlockRegs<D, FP8, NT>& r, int tid) {
-  using C = PCfg<D, FP8>;
+  using U = Units<D, FP8, NT>;
   using S = Stage<D>;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D, FP8, NT>::kUnits; ++i) {
+  for (int i = 0; i < U::kPerThread; ++i) {
     const int u = tid + NT * i;
-    if (u >= C::kBlockUnits) break;
-    const int row = u / C::kRowUnits, unit = u % C::kRowUnits;
+    if (u >= U::kBlockUnits) break;
+    const int row = u / U::kRowUnits, unit = u % U::kRowUnits;
     uint8_t* kd = st.k + row * S::kKStride;
     uint8_t* vd = st.v + row * S::kVStride;
-    if constexpr (FP8) {  // 16 codes -> 32 bytes of bf16
+    if constexpr (FP8) {  // each dword of 4 codes -> 8 bytes of bf16
+      uvec<2 * U::kWords> kw, vw;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const u32x2 ka = fp8x4_to_bf16(r.k[i][2 * half]), kb2 = fp8x4_to_bf16(r.k[i][2 * half + 1]);
-        const u32x2 va = fp8x4_to_bf16(r.v[i][2 * half]), vb = fp8x4_to_bf16(r.v[i][2 * half + 1]);
-        *reinterpret_cast<u32x4*>(kd + 32 * unit + 16 * half) = u32x4{ka[0], ka[1], kb2[0], kb2[1]};
-        *reinterpret_cast<u32x4*>(vd + 32 * unit + 16 * half) = u32x4{va[0], va[1], vb[0], vb[1]};
+      for (int w = 0; w < U::kWords; ++w) {
+        const u32x2 ka = fp8x4_to_bf16(r.k[i][w]), va = fp8x4_to_bf16(r.v[i][w]);
+        kw[2 * w] = ka[0];
+        kw[2 * w + 1] = ka[1];
+        vw[2 * w] = va[0];
+        vw[2 * w + 1] = va[1];
       }
+      *reinterpret_cast<uvec<2 * U::kWords>*>(kd + 2 * U::kBytes * unit) = kw;
+      *reinterpret_cast<uvec<2 * U::kWords>*>(vd + 2 * U::kBytes * unit) = vw;
     } else {
       *reinterpret_cast<u32x4*>(kd + 16 * unit) = r.k[i];
       *reinterpret_cast<u32x4*>(vd + 16 * unit) = r.v[i];
@@ -233,6 +256,13 @@ __device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, x);
 }
 
+// A load whose address is the same in every lane, through the scalar data cache (the
+// constant address space): it is waited for apart from the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* ptr, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)(ptr))[i];
+}
+
 __device__ __forceinline__ float max8(const float (&a)[8]) {
   return fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]),
                fmaxf(fmaxf(fmaxf(a[3], a[4]), a[5]), fmaxf(a[6], a[7])));
@@ -246,38 +276,62 @@ struct RowState {
   float m, negm, l;
 };
 
-// One 32-key block for this wave's 16 query tokens and HPW heads (lane (n, gq): query
-// n). diag: the block reaches past some token's position, so keys j > pos are masked.
-// Per key the exponent argument a = s c - m is formed first; the row maximum needs a
-// cross-lane reduction only when some lane sees a > 8 (m must be raised), a rare
-// branch. The rare cases (masking, raising the maximum, the low part of P) are
-// uniform branches inside one body, so the accumulators keep one register assignment.
-template <int D, bool FP8, int HPW>
-__device__ __forceinline__ void attend_block(const Stage<D>& st,
-                                             const u32x4 (&qf)[HPW][PCfg<D, FP8>::kSteps],
-                                             f32x4 (&acc)[HPW][PCfg<D, FP8>::kDimBlocks],
-                                             RowState (&rs)[HPW], bool diag, int j0, int pos, int n,
-                                             int gq, const float (&c)[2], const float (&v_mul)[2]) {
-  using C = PCfg<D, FP8>;
+// K operands of one staged block: key 16h + n, dims op_dim(s, gq, 0..7).
+template <int D>
+__device__ __forceinline__ void read_k(const Stage<D>& st, int n, int gq,
+                                       u32x4 (&kop)[2][PCfg<D, false>::kSteps]) {
   using S = Stage<D>;
-  // K operands: key 16h + n, dims op_dim(s, gq, 0..7).
   const uint8_t* kbase = st.k + n * S::kKStride + 16 * gq;
-  u32x4 kop[2][C::kSteps];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s)
+    for (int s = 0; s < PCfg<D, false>::kSteps; ++s)
       kop[h][s] = *reinterpret_cast<const u32x4*>(kbase + 16 * h * S::kKStride + 64 * s);
-  // Raw scores S^T: lane (n, gq) holds keys j0 + 16h + 4gq + v of query n.
-  f32x4 sacc[HPW][2];
+}
+
+// Raw scores S^T = K . Q^T of one block: lane (n, gq) gets keys 16h + 4gq + v of query n.
+template <int D, int HPW>
+__device__ __forceinline__ void score_block(const u32x4 (&kop)[2][PCfg<D, false>::kSteps],
+                                            const u32x4 (&qf)[HPW][PCfg<D, false>::kSteps],
+                                            f32x4 (&sacc)[HPW][2]) {
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       sacc[hh][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) sacc[hh][h] = mfma_bf16(kop[h][s], qf[hh][s], sacc[hh][h]);
+      for (int s = 0; s < PCfg<D, false>::kSteps; ++s) sacc[hh][h] = mfma_bf16(kop[h][s], qf[hh][s], sacc[hh][h]);
     }
+}
+
+// V^T operands of one staged block: dims 16bl + n, keys 4gq + 0..3 then 16 + 4gq + 0..3
+// (two transposing reads; lane (n, gq) addresses row 4gq + n / 4, dims 16bl + 4 (n % 4)).
+template <int D>
+__device__ __forceinline__ void read_v(const Stage<D>& st, int n, int gq,
+                                       u32x4 (&vop)[PCfg<D, false>::kDimBlocks]) {
+  using S = Stage<D>;
+  const uint8_t* vbase = st.v + (4 * gq + (n >> 2)) * S::kVStride + 8 * (n & 3);
+#pragma unroll
+  for (int bl = 0; bl < PCfg<D, false>::kDimBlocks; ++bl) {
+    const u32x2 lo = read_tr16(vbase + 32 * bl);
+    const u32x2 hi = read_tr16(vbase + 16 * S::kVStride + 32 * bl);
+    vop[bl] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// Online softmax of one block's scores for this wave's 16 query tokens and HPW heads
+// (lane (n, gq): query n), first part. diag: the block reaches past some token's
+// position, so keys j > pos are masked. Per key the exponent argument a = s c - m is
+// formed; the row maximum needs a cross-lane reduction only when some lane sees a > 8
+// (m must be raised), a rare branch that rescales the accumulators. Out: the
+// arguments and each head's largest argument on this lane.
+template <int D, bool FP8, int HPW>
+__device__ __forceinline__ void softmax_args(bool diag, int j0, int pos, int gq,
+                                             f32x4 (&sacc)[HPW][2],
+                                             f32x4 (&acc)[HPW][PCfg<D, FP8>::kDimBlocks],
+                                             RowState (&rs)[HPW], const float (&c)[2],
+                                             float (&arg)[HPW][8], float (&amax)[HPW]) {
+  using C = PCfg<D, FP8>;
   if (diag) {
     const int lim = pos - j0 - 4 * gq;  // key 16h + v of this lane is visible iff 16h + v <= lim
 #pragma unroll
@@ -289,7 +343,6 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
           if (16 * h + v > lim) sacc[hh][h][v] = -INFINITY;
   }
   // Exponent arguments a = s c - m (masked keys: -inf, since c > 0) and their lane max.
-  float arg[HPW][8], amax[HPW];
   bool raise = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -322,13 +375,18 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
       amax[hh] = max8(arg[hh]);
     }
   }
-  // Probabilities p = 2^a (times the V scale for FP8), this lane's sums, and P^T
-  // packed to bf16. The low-part test uses this lane's largest p and sum: if a row's
-  // largest p exceeds a quarter of the row's sum after the block, the lane that holds
-  // it sees 3 p > (its sum before the block).
-  float pv[HPW][8];
-  u32x4 ph[HPW];
-  bool low = false;
+}
+
+// Second part: probabilities p = 2^a (times the V scale for FP8), this lane's sums, P^T
+// packed to bf16 in ph, and whether the low bf16 part of P must be multiplied into V
+// as well. The low-part test uses this lane's largest p and sum: if a row's largest p
+// exceeds a quarter of the row's sum after the block, the lane that holds it sees
+// 3 p > (its sum before the block).
+template <bool FP8, int HPW>
+__device__ __forceinline__ void softmax_probs(const float (&arg)[HPW][8], const float (&amax)[HPW],
+                                              RowState (&rs)[HPW], const float (&v_mul)[2],
+                                              float (&pv)[HPW][8], u32x4 (&ph)[HPW], bool& low) {
+  low = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     low |= kLowPartTest * __builtin_amdgcn_exp2f(amax[hh]) > rs[hh].l;
@@ -346,20 +404,18 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
 #pragma unroll
     for (int e = 0; e < 4; ++e) ph[hh][e] = pack_bf16(pv[hh][2 * e], pv[hh][2 * e + 1]);
   }
-  // V^T operands: dims 16bl + n, keys 4gq + 0..3 then 16 + 4gq + 0..3 (two
-  // transposing reads; lane (n, gq) addresses row 4gq + n / 4, dims 16bl + 4 (n % 4)).
-  const uint8_t* vbase = st.v + (4 * gq + (n >> 2)) * S::kVStride + 8 * (n & 3);
-  u32x4 vop[C::kDimBlocks];
-#pragma unroll
-  for (int bl = 0; bl < C::kDimBlocks; ++bl) {
-    const u32x2 lo = read_tr16(vbase + 32 * bl);
-    const u32x2 hi = read_tr16(vbase + 16 * S::kVStride + 32 * bl);
-    vop[bl] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
+}
+
+// O^T += V^T . P^T for one block, plus the low bf16 part of P where asked.
+template <int D, int HPW>
+__device__ __forceinline__ void pv_block(const u32x4 (&vop)[PCfg<D, false>::kDimBlocks],
+                                         const float (&pv)[HPW][8], const u32x4 (&ph)[HPW], bool low,
+                                         f32x4 (&acc)[HPW][PCfg<D, false>::kDimBlocks]) {
+  constexpr int kDimBlocks = PCfg<D, false>::kDimBlocks;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int bl = 0; bl < C::kDimBlocks; ++bl) acc[hh][bl] = mfma_bf16(vop[bl], ph[hh], acc[hh][bl]);
+    for (int bl = 0; bl < kDimBlocks; ++bl) acc[hh][bl] = mfma_bf16(vop[bl], ph[hh], acc[hh][bl]);
   if (__builtin_amdgcn_ballot_w64(low)) {
     // The low part goes through a fresh accumulator and is added in place, so the
     // accumulators keep their registers whichever way this branch goes.
@@ -371,7 +427,7 @@ __device__ __forceinline__ void attend_block(const Stage<D>& st,
       for (int e = 0; e < 4; ++e)
         pl[e] = pack_bf16(pv[hh][2 * e] - bf16_lo(ph[hh][e]), pv[hh][2 * e + 1] - bf16_hi(ph[hh][e]));
 #pragma unroll
-      for (int bl = 0; bl < C::kDimBlocks; ++bl)
+      for (int bl = 0; bl < kDimBlocks; ++bl)
         acc[hh][bl] += mfma_bf16(vop[bl], pl, f32x4{0.f, 0.f, 0.f, 0.f});
     }
   }
@@ -384,7 +440,7 @@ void prefill_kernel(const PrefillParams p) {
   using W = WaveCfg<GWI>;
   constexpr int HPW = W::kHeadsPerWave;
   constexpr int NT = W::kThreads;
-  __shared__ Stage<D> stage[2];
+  __shared__ Stage<D> stage[3];
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slice = wid & 3, head_pair = wid >> 2;
@@ -447,17 +503,32 @@ void prefill_kernel(const PrefillParams p) {
     rs[hh] = RowState{-INFINITY, INFINITY, 0.f};
   }
 
-  // Double-buffered stage: block kb is written into stage[kb & 1] while the other
-  // buffer may still be read; the one barrier per block separates both uses. The
-  // block-table entries (and FP8 page scales) are loaded one block ahead of the K/V
-  // loads that use them.
+  // Triple-buffered stage, one barrier per block. In step kb the workgroup stages block
+  // kb + 1 and each wave then reads block kb + 1's K operands and block kb's V operands,
+  // so block kb + 1's score products are issued around block kb's softmax and the LDS
+  // reads overlap vector and matrix work. A buffer written in step kb last held block
+  // kb - 2, whose reads all ended before the barrier of step kb - 1. The K/V loads run
+  // one block ahead of the staging, the block-table entries (and FP8 page scales) one
+  // block ahead of the loads that use them.
   using R = BlockRegs<D, FP8, NT>;
   const int last_page = (L - 1) / p.page_size;
   R regs;
   walk_init<D, FP8, NT>(regs, p.page_size, tid);
   block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
   load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, 0, L, tid);
-  if (nblocks > 1) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+  stage_block<D, FP8, NT>(stage[0], regs, tid);
+  if (nblocks > 1) {
+    block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+    load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, 1, L, tid);
+    if (nblocks > 2) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+  }
+  __syncthreads();
+  f32x4 sacc[HPW][2] = {};
+  if (wave_blocks > 0) {
+    u32x4 kop[2][C::kSteps];
+    read_k<D>(stage[0], n, gq, kop);
+    score_block<D, HPW>(kop, qf, sacc);
+  }
   // FP8 page scales of the block being computed, one per 16-key half (a half lies in
   // one page; the two may differ when pages are shorter than 32 keys or not aligned to
   // blocks), and the physical pages of the next block's halves.
@@ -469,7 +540,7 @@ void prefill_kernel(const PrefillParams p) {
   float ksc[2] = {1.f, 1.f}, vsc[2] = {1.f, 1.f};
   int scale_page[2] = {0, 0};
   int hpg[2] = {0, 0}, hrow[2] = {0, 0};  // logical page and row of half h's first key
-  auto half_phys = [&](int h) { return bt[min(hpg[h], last_page)]; };
+  auto half_phys = [&](int h) { return load_uniform(bt, min(hpg[h], last_page)); };
   auto half_advance = [&](int h) {  // by one block of keys
     hrow[h] += kBlockKeys;
     while (hrow[h] >= p.page_size) {
@@ -479,57 +550,77 @@ void prefill_kernel(const PrefillParams p) {
   };
   const int scale_halves = (p.page_size % kBlockKeys == 0) ? 1 : 2;
   if constexpr (FP8) {
-    for (int h = 0; h < scale_halves; ++h) {
-      hpg[h] = (16 * h) / p.page_size;
-      hrow[h] = 16 * h - hpg[h] * p.page_size;
-      const int64_t sidx = static_cast<int64_t>(half_phys(h)) * p.num_kv_heads + g;
-      ksc[h] = p.k_scale[sidx];
-      vsc[h] = p.v_scale[sidx];
-      half_advance(h);
-      scale_page[h] = half_phys(h);
-    }
-    if (scale_halves == 1) {
-      ksc[1] = ksc[0];
-      vsc[1] = vsc[0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h < scale_halves) {
+        hpg[h] = (16 * h) / p.page_size;
+        hrow[h] = 16 * h - hpg[h] * p.page_size;
+        const int64_t sidx = static_cast<int64_t>(half_phys(h)) * p.num_kv_heads + g;
+        ksc[h] = load_uniform(p.k_scale, sidx);
+        vsc[h] = load_uniform(p.v_scale, sidx);
+        half_advance(h);
+        scale_page[h] = half_phys(h);
+      }
     }
   }
+  int cur = 0, nxt = 1;  // stage buffers of blocks kb and kb + 1
   for (int kb = 0; kb < nblocks; ++kb) {
-    Stage<D>& st = stage[kb & 1];
-    stage_block<D, FP8, NT>(st, regs, tid);
-    __syncthreads();
     float ksc_next[2] = {1.f, 1.f}, vsc_next[2] = {1.f, 1.f};
     if (kb + 1 < nblocks) {
-      load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, kb + 1, L, tid);
-      if (kb + 2 < nblocks) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+      stage_block<D, FP8, NT>(stage[nxt], regs, tid);
+      __syncthreads();
+      if (kb + 2 < nblocks) {
+        load_block<D, FP8, NT>(regs, p.k_cache, p.v_cache, page_bytes, head_off, kb + 2, L, tid);
+        if (kb + 3 < nblocks) block_pages<D, FP8, NT>(regs, bt, last_page, p.page_size, tid);
+      }
       if constexpr (FP8) {
-        for (int h = 0; h < scale_halves; ++h) {
-          const int64_t sidx = static_cast<int64_t>(scale_page[h]) * p.num_kv_heads + g;
-          ksc_next[h] = p.k_scale[sidx];
-          vsc_next[h] = p.v_scale[sidx];
-          if (kb + 2 < nblocks) {
-            half_advance(h);
-            scale_page[h] = half_phys(h);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h < scale_halves) {
+            const int64_t sidx = static_cast<int64_t>(scale_page[h]) * p.num_kv_heads + g;
+            ksc_next[h] = load_uniform(p.k_scale, sidx);
+            vsc_next[h] = load_uniform(p.v_scale, sidx);
+            if (kb + 2 < nblocks) {
+              half_advance(h);
+              scale_page[h] = half_phys(h);
+            }
           }
-        }
-        if (scale_halves == 1) {
-          ksc_next[1] = ksc_next[0];
-          vsc_next[1] = vsc_next[0];
         }
       }
     }
     if (kb < wave_blocks) {
       const int j0 = kb * kBlockKeys;
+      const bool diag = j0 + kBlockKeys - 1 > wave_first_pos;
       // c > 0 keeps masked keys at a = -inf (a zero scale acts as the smallest normal one).
+      // With one scale lookup per block the second half takes the first half's scales.
+      const float ksc1 = scale_halves == 2 ? ksc[1] : ksc[0];
+      const float vs[2] = {vsc[0], scale_halves == 2 ? vsc[1] : vsc[0]};
       const float c[2] = {fmaxf(qk_log2 * ksc[0], 1.17549435e-38f),
-                          fmaxf(qk_log2 * ksc[1], 1.17549435e-38f)};
-      attend_block<D, FP8, HPW>(st, qf, acc, rs, j0 + kBlockKeys - 1 > wave_first_pos, j0, pos, n,
-                                gq, c, vsc);
+                          fmaxf(qk_log2 * ksc1, 1.17549435e-38f)};
+      float pv[HPW][8];
+      u32x4 ph[HPW];
+      bool low;
+      u32x4 vop[C::kDimBlocks];
+      float arg[HPW][8], amax[HPW];
+      softmax_args<D, FP8, HPW>(diag, j0, pos, gq, sacc, acc, rs, c, arg, amax);
+      // The next block's scores, issued among this block's exponentials (unused after
+      // the wave's last block, whose next buffer then holds an earlier block).
+      {
+        u32x4 kop[2][C::kSteps];
+        read_k<D>(stage[nxt], n, gq, kop);
+        score_block<D, HPW>(kop, qf, sacc);
+      }
+      softmax_probs<FP8, HPW>(arg, amax, rs, vs, pv, ph, low);
+      read_v<D>(stage[cur], n, gq, vop);
+      pv_block<D, HPW>(vop, pv, ph, low, acc);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       ksc[h] = ksc_next[h];
       vsc[h] = vsc_next[h];
     }
+    cur = nxt;
+    nxt = nxt == 2 ? 0 : nxt + 1;
   }
 
   // Rows to the output: lane (n, gq) holds dims 16bl + 4gq + v of query n; the row's
