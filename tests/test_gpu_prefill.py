@@ -100,6 +100,9 @@ SMALL = [
          q=[1, 47, 49, 190], pre=[0, 1, 95, 129]),
     dict(id="fp8_g8_d128_p32", c=cfg(kv_format="fp8", page_size=32, num_q_heads=8), q=[100, 33],
          pre=[31, 300]),
+    # Four-head groups at D = 64: each of the 512 threads widens one 4-byte unit of a block.
+    dict(id="fp8_g4_d64_p16", c=cfg(kv_format="fp8", page_size=16, head_dim=64), q=[3, 64, 97, 1],
+         pre=[0, 33, 15, 95]),
 ]
 
 
