@@ -25,13 +25,6 @@
 namespace pkv {
 namespace {
 
-// Waves per workgroup: (page 0, 1) x (K, V); one new token per request touches one
-// page, so two waves (page 0's K and V) do then.
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
@@ -116,7 +109,8 @@ __device__ __forceinline__ void rotate4(float (&x1)[4], float (&x2)[4], const fl
 // more query heads or draft tokens, in a loop afterwards).
 constexpr int kQPre = 2;
 
-// One workgroup of four waves per (request b, kv head g). Wave 2p + kind writes the
+// One workgroup of kWaves waves per (request b, kv head g): four, or two when each
+// request appends one token (which touches one page only). Wave 2p + kind writes the
 // new rows of touched page p (0: the page of the first new token, 1: the next one,
 // if touched) of K (kind 0, rotated) or V (kind 1); each lane holds four rotation
 // pairs (i0 .. i0+3 and the same + D/2 of one row), so the page's largest |value|
