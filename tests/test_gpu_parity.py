@@ -154,6 +154,38 @@ def test_small_cases_match_oracle(case):
     check(inp, out, lse, tag=case["id"])
 
 
+def random_case(seed):
+    """A small random decode batch from ``default_rng(seed)``: head group and draft
+    tokens (up to 64 rows per kv head), kv heads, head dim, page size, format, lengths,
+    a fixed tile (a multiple of the format's quantum) or the automatic one, workers."""
+    rng = np.random.default_rng(2000 + seed)
+    Tq = int(rng.integers(1, 5))
+    G = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8, 12, 16, 32, 64) if g * Tq <= 64]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    P = int(rng.choice([16, 32, 48, 64]))
+    fmt = str(rng.choice(["bf16", "fp8"]))
+    c = cfg(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=int(rng.choice([64, 128])),
+            page_size=P, kv_format=fmt, q_len=Tq)
+    B = int(rng.integers(1, 9))
+    sl = [int(x) for x in rng.integers(Tq, 3000, B)]
+    quantum = P if fmt == "bf16" else P * 64 // int(np.gcd(P, 64))
+    T = 0 if rng.random() < 0.3 else quantum * int(rng.integers(1, 9))
+    W = int(rng.integers(1, 13))
+    return c, sl, T, W
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small_shapes_match_oracle(seed):
+    c, sl, T, W = random_case(seed)
+    inp = synth.make_inputs(c, seed=40 + seed, poison=True, slack_pages=2, seq_lens=sl)
+    tag = "random %d: B=%d Tq=%d G=%d Hkv=%d D=%d P=%d %s T=%d W=%d" % (
+        seed, inp.batch, inp.q_len, inp.num_q_heads // inp.num_kv_heads, inp.num_kv_heads,
+        inp.head_dim, inp.page_size, inp.kv_format, T, W)
+    log(tag)
+    out, lse, _ = run_decode(inp, T, W)
+    check(inp, out, lse, tag=tag)
+
+
 @pytest.mark.parametrize("name", ["llama8b", "mixed", "long", "fp8_spec"])
 def test_full_size_workloads(name):
     """The full workloads in the launch configuration the bench times (automatic tile

@@ -115,6 +115,35 @@ def test_small_batches_match_the_oracle(case):
     compare(p, out, lse, ref_out, ref_lse, case["id"])
 
 
+def random_case(seed):
+    """A small random prefill batch: head group, kv heads, head dim, page size, format,
+    query lengths and prefixes drawn from ``default_rng(seed)``."""
+    rng = np.random.default_rng(1000 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 12]))  # the group sizes prefill supports
+    Hkv = int(rng.choice([1, 2]))
+    fmt = str(rng.choice(["bf16", "fp8"]))
+    c = cfg(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=int(rng.choice([64, 128])),
+            page_size=int(rng.choice([16, 32, 48, 64])), kv_format=fmt)
+    B = int(rng.integers(1, 5))
+    q = [int(x) for x in rng.integers(1, 200, B)]
+    pre = [int(x) for x in rng.integers(0, 300, B)]
+    return c, q, pre
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_batches_match_the_oracle(seed):
+    """Random shapes: tiles of 1-4 blocks and longer, every head-group width (one, two or
+    four heads per item), both formats, pages of 16-64 tokens, against the oracle."""
+    c, q, pre = random_case(seed)
+    p = synth.make_prefill_inputs(c, seed=30 + seed, q_lens=q, prefix=pre, poison=True,
+                                  slack_pages=2)
+    out, lse, _ = run_prefill(p)
+    ref_out, ref_lse = prefill_attention(p)
+    compare(p, out, lse, ref_out, ref_lse, "random %d: %s q=%s pre=%s" % (
+        seed, {k: c[k] for k in ("num_q_heads", "num_kv_heads", "head_dim", "page_size",
+                                 "kv_format")}, q, pre))
+
+
 def test_without_lse_the_output_is_the_same():
     p = synth.make_prefill_inputs(cfg(), seed=12, q_lens=[70, 9], prefix=[5, 60])
     dev = device_prefill(p)
