@@ -114,6 +114,38 @@ def test_small_cases_match_oracle(case, device_plan):
     check_sparse(inp, mask, out, lse, tag=case["id"])
 
 
+def random_case(seed):
+    """A random block-sparse batch from ``default_rng(seed)``: shape as in the random
+    decode cases, a keep fraction, a fixed or automatic tile, workers, host or device
+    plan."""
+    rng = np.random.default_rng(4000 + seed)
+    Tq = int(rng.integers(1, 5))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16, 32) if g * Tq <= 64]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    P = int(rng.choice([16, 32, 48, 64]))
+    fmt = str(rng.choice(["bf16", "fp8"]))
+    c = cfg(num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=int(rng.choice([64, 128])),
+            page_size=P, kv_format=fmt, q_len=Tq)
+    sl = [int(x) for x in rng.integers(Tq, 2500, int(rng.integers(1, 9)))]
+    quantum = P if fmt == "bf16" else P * 64 // int(np.gcd(P, 64))
+    T = 0 if rng.random() < 0.4 else quantum * int(rng.integers(1, 6))
+    return (c, sl, float(rng.choice([0.1, 0.3, 0.6, 1.0])), T, int(rng.integers(1, 12)),
+            bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shapes_match_oracle(seed):
+    c, sl, keep, T, W, device_plan = random_case(seed)
+    inp = synth.make_inputs(c, seed=70 + seed, poison=True, slack_pages=2, seq_lens=sl)
+    mask = synth.make_block_mask(inp, keep, seed=80 + seed)
+    tag = "random %d: B=%d Tq=%d Hq=%d Hkv=%d D=%d P=%d %s keep=%.1f T=%d W=%d device_plan=%s" % (
+        seed, inp.batch, inp.q_len, inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+        inp.kv_format, keep, T, W, device_plan)
+    log(tag)
+    out, lse, _ = run_sparse(inp, mask, T=T, W=W, device_plan=device_plan)
+    check_sparse(inp, mask, out, lse, tag=tag)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_host_and_device_plans_agree_bitwise(fmt):
     c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2, num_q_heads=16, num_kv_heads=4)

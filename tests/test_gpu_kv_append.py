@@ -116,6 +116,38 @@ def test_append_matches_oracle(case):
     assert_same(inp, dev, q_gpu, q_ref, case["id"])
 
 
+def random_case(seed):
+    """A random append from ``default_rng(seed)``: format, page size, head dim, heads,
+    new tokens (1-4), rotation or not, lengths, and which groups' new rows are scaled far
+    beyond their pages' range."""
+    rng = np.random.default_rng(3000 + seed)
+    Tq = int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    c = cfg(kv_format=str(rng.choice(["bf16", "fp8"])), page_size=int(rng.choice([16, 32, 48, 64])),
+            head_dim=int(rng.choice([64, 128])), num_kv_heads=Hkv,
+            num_q_heads=Hkv * int(rng.choice([1, 2, 4, 8])), q_len=Tq)
+    lens = [int(x) for x in rng.integers(Tq, 700, int(rng.integers(1, 40)))]
+    rope = bool(rng.random() < 0.6)
+    far = rng.random((len(lens), Hkv)) < float(rng.choice([0.0, 0.3, 1.0]))
+    return c, lens, rope, np.where(far, float(rng.choice([10.0, 3e3])), 1.0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_appends_match_oracle(seed):
+    c, lens, rope_on, scale = random_case(seed)
+    inp = synth.make_inputs(c, seed=50 + seed, slack_pages=2, seq_lens=lens)
+    k_new, v_new, q = synth.new_token_rows(inp, seed=60 + seed, scale=scale)
+    rope = synth.rope_tables(inp.block_table.shape[1] * inp.page_size, inp.head_dim) if rope_on else None
+    dev = device_inputs(inp)
+    tag = "random %d: B=%d Tq=%d Hq=%d Hkv=%d D=%d P=%d %s rope=%s" % (
+        seed, inp.batch, inp.q_len, inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+        inp.kv_format, rope_on)
+    log(tag)
+    q_gpu = gpu_append(inp, dev, k_new, v_new, q, rope)
+    q_ref = oracle_append(inp, k_new, v_new, q, rope)
+    assert_same(inp, dev, q_gpu, q_ref, tag)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_repeated_appends_match_oracle(fmt):
     c = cfg(kv_format=fmt, page_size=64 if fmt == "fp8" else 16, q_len=2)
