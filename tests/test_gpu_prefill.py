@@ -223,15 +223,35 @@ def test_empty_requests_are_skipped():
     assert out.shape[0] == 0 and lse.shape[0] == 0
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("scale", [-0.07, 0.0])
-def test_negative_and_zero_scale(scale):
-    """A negative softmax scale is taken exactly (Q's sign flipped); a zero scale gives
-    the mean of the visible V rows."""
-    p = synth.make_prefill_inputs(cfg(), seed=23, q_lens=[40, 9], prefix=[30, 0])
+def test_negative_and_zero_scale(scale, fmt):
+    """A negative softmax scale is taken exactly (Q's sign flipped; with FP8 K, before
+    the query is split into its two e4m3 terms); a zero scale gives the mean of the
+    visible V rows."""
+    c = cfg() if fmt == "bf16" else cfg(kv_format="fp8", page_size=64)
+    p = synth.make_prefill_inputs(c, seed=23, q_lens=[40, 9], prefix=[30, 0])
     p.cache.scale = np.float32(scale)
     out, lse, _ = run_prefill(p)
     ref_out, ref_lse = prefill_attention(p)
-    compare(p, out, lse, ref_out, ref_lse, "scale_%g" % scale)
+    compare(p, out, lse, ref_out, ref_lse, "scale_%g_%s" % (scale, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_query_rows_of_any_magnitude(fmt):
+    """Query rows scaled by powers of two from 2^-24 (near-uniform weights) to 2^5 (sharp
+    softmax, the running maximum raised often), and all-zero rows: with FP8 K each row
+    enters the FP8 product as two e4m3 terms under its own power of two."""
+    c = cfg() if fmt == "bf16" else cfg(kv_format="fp8", page_size=64)
+    p = synth.make_prefill_inputs(c, seed=31, q_lens=[70, 129, 3], prefix=[20, 0, 250])
+    q = (p.q.astype(np.uint32) << np.uint32(16)).view(np.float32)  # [tokens, Hq, D]
+    rows = np.arange(q.shape[0] * q.shape[1]).reshape(q.shape[0], q.shape[1])
+    factor = 2.0 ** np.array([-24.0, -8.0, 0.0, 3.0, 5.0])[rows % 5]
+    factor[rows % 7 == 6] = 0.0
+    p.q = synth.gen.f32_to_bf16_bits(q * factor[:, :, None].astype(np.float32))
+    out, lse, _ = run_prefill(p)
+    ref_out, ref_lse = prefill_attention(p)
+    compare(p, out, lse, ref_out, ref_lse, "q_magnitudes_%s" % fmt)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
