@@ -254,7 +254,7 @@ def prefill_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if c.kv_format == "bf16" else "fp8 KV (QK^T on fp8 MFMA, P.V on bf16 MFMA)",
+        "dtype": "bf16" if c.kv_format == "bf16" else "fp8 KV, bf16 MFMA",
         "data": "synthetic",
         "config": {
             "workload": cfg["desc"],

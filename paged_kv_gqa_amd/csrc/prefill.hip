@@ -35,13 +35,9 @@
 //   work overlap inside one wave. The stage is triple-buffered with one barrier per
 //   block; the K/V loads for the stage run one block ahead, the block-table entries
 //   one block earlier still.
-// FP8 (e4m3fn) K codes are staged as they are and feed gfx950's FP8 matrix instruction
-// (v_mfma_scale_f32_16x16x128_f8f6f4, one per 16-key half and query term): each query
-// row enters as two e4m3 terms with a power-of-two row scale (q_to_fp8), so K is
-// neither widened nor read from LDS at 16 bits. FP8 V bytes are widened to bf16
-// exactly when staged, once per workgroup and spread over all of its threads. Each
-// 16-key half of a block lies in one page, whose K scale multiplies that half's scores
-// and whose V scale its P.
+// FP8 (e4m3fn) K/V bytes are widened to bf16 exactly when staged, once per workgroup
+// and spread over all of its threads; each 16-key half of a block lies in one page,
+// whose K scale multiplies that half's scores and whose V scale its P.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -55,8 +51,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileTokens = 64;     // query tokens per work item (4 token slices x 16)
 constexpr int kBlockKeys = 32;
@@ -73,13 +67,6 @@ constexpr float kLowPartTest = 3.f;
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// D += A . B over 128 e4m3fn values per row and column (A: row l % 16, B: column
-// l % 16; the four 16-lane groups hold the k-values, in the same order for A and B),
-// with unit block scales (E8M0 code 127 = 2^0).
-__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
@@ -112,46 +99,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Head dim of byte e (0..31) of lane group gq's FP8 score operand: 32 consecutive dims
-// at D = 128, 16 at D = 64 (bytes 16..31 are zero there).
-template <int D>
-__device__ __forceinline__ int fp8_dim(int gq, int e) { return (D / 4) * gq + e; }
-
-// One query row (this lane's NV values of it; the row's four lanes together hold all of
-// it) as two e4m3fn terms for the FP8 score product. With the row's largest |q| in
-// [2^(E-1), 2^E), x = q 2^(8-E) is exact and below 256; hi = e4m3(x) and lo = e4m3(x - hi)
-// (x - hi is exact in fp32), so hi + lo is within max(2^-8 |x|, 2^-10) of x, where 2^-10
-// (a subnormal term's rounding) is below 2^-17 of the row's largest |x| (at least 128).
-// Returns 2^(E-8), which brings the products back to q's scale.
-template <int NV>
-__device__ __forceinline__ float q_to_fp8(const float (&x)[NV], i32x8& hi, i32x8& lo) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  int e;
-  (void)frexpf(group_max(amax), &e);  // 0 for an all-zero row
-  e = max(e, -100);
-  const float up = ldexpf(1.f, 8 - e);
-  int h[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < NV; i += 4) {
-    const float a0 = x[i] * up, a1 = x[i + 1] * up, a2 = x[i + 2] * up, a3 = x[i + 3] * up;
-    s16x2 w = {0, 0};
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a0, a1, 1.f, false);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a2, a3, 1.f, true);
-    const unsigned hw = __builtin_bit_cast(unsigned, w);
-    const u32x2 hb = fp8x4_to_bf16(hw);  // hi back to floats, exactly
-    s16x2 v = {0, 0};
-    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, a0 - bf16_lo(hb[0]), a1 - bf16_hi(hb[0]), 1.f, false);
-    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, a2 - bf16_lo(hb[1]), a3 - bf16_hi(hb[1]), 1.f, true);
-    h[i / 4] = static_cast<int>(hw);
-    l[i / 4] = __builtin_bit_cast(int, v);
-  }
-  hi = i32x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
-  lo = i32x8{l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]};
-  return ldexpf(1.f, e - 8);
-}
-
 // Heads per work item GWI (1, 2, 4); each wave takes 16 tokens x HPW heads.
 template <int GWI>
 struct WaveCfg {
@@ -171,14 +118,13 @@ struct PCfg {
 // Head dimension of k-step s, lane group gq, element e of the S^T operands.
 __device__ __forceinline__ int op_dim(int s, int gq, int e) { return 32 * s + 8 * gq + e; }
 
-// LDS (bytes): K rows [32] as bf16 with a stride of 2D + 16, or as FP8 codes with a
-// stride of D + 16 (16 lanes reading one 16-byte unit of rows n = 0..15 hit disjoint
-// bank groups), and V rows [32] as bf16 with a stride of 2D + 32 (the four rows of a
-// transposing read hit disjoint bank groups). Each lane reads at one base address plus
-// constant offsets.
-template <int D, bool FP8>
+// LDS (bytes), bf16 rows: K rows [32] of stride 2D + 16 (16 lanes reading one 16-byte
+// unit of rows n = 0..15 hit disjoint bank groups) and V rows [32] of stride 2D + 32
+// (the four rows of a transposing read hit disjoint bank groups). Each lane reads at
+// one base address plus constant offsets.
+template <int D>
 struct Stage {
-  static constexpr int kKStride = (FP8 ? D : 2 * D) + 16;
+  static constexpr int kKStride = 2 * D + 16;
   static constexpr int kVStride = 2 * D + 32;
   alignas(16) uint8_t k[kBlockKeys * kKStride];
   alignas(16) uint8_t v[kBlockKeys * kVStride];
@@ -270,12 +216,11 @@ __device__ __forceinline__ void load_block(BlockRegs<D, FP8, NT>& r, const uint8
   }
 }
 
-// K and V rows into LDS, row-major: K as stored (FP8 codes feed the FP8 matrix
-// instruction directly), V as bf16 (FP8 codes widened exactly).
+// K and V rows into LDS as bf16 (fp8 widened exactly), row-major.
 template <int D, bool FP8, int NT>
-__device__ __forceinline__ void stage_block(Stage<D, FP8>& st, const BlockRegs<D, FP8, NT>& r, int tid) {
+__device__ __forceinline__ void stage_block(Stage<D>& st, const BlockRegs<D, FP8, NT>& r, int tid) {
   using U = Units<D, FP8, NT>;
-  using S = Stage<D, FP8>;
+  using S = Stage<D>;
 #pragma unroll
   for (int i = 0; i < U::kPerThread; ++i) {
     const int u = tid + NT * i;
@@ -283,15 +228,17 @@ __device__ __forceinline__ void stage_block(Stage<D, FP8>& st, const BlockRegs<D
     const int row = u / U::kRowUnits, unit = u % U::kRowUnits;
     uint8_t* kd = st.k + row * S::kKStride;
     uint8_t* vd = st.v + row * S::kVStride;
-    if constexpr (FP8) {  // each dword of 4 V codes -> 8 bytes of bf16
-      uvec<2 * U::kWords> vw;
+    if constexpr (FP8) {  // each dword of 4 codes -> 8 bytes of bf16
+      uvec<2 * U::kWords> kw, vw;
 #pragma unroll
       for (int w = 0; w < U::kWords; ++w) {
-        const u32x2 va = fp8x4_to_bf16(r.v[i][w]);
+        const u32x2 ka = fp8x4_to_bf16(r.k[i][w]), va = fp8x4_to_bf16(r.v[i][w]);
+        kw[2 * w] = ka[0];
+        kw[2 * w + 1] = ka[1];
         vw[2 * w] = va[0];
         vw[2 * w + 1] = va[1];
       }
-      *reinterpret_cast<uvec<U::kWords>*>(kd + U::kBytes * unit) = r.k[i];
+      *reinterpret_cast<uvec<2 * U::kWords>*>(kd + 2 * U::kBytes * unit) = kw;
       *reinterpret_cast<uvec<2 * U::kWords>*>(vd + 2 * U::kBytes * unit) = vw;
     } else {
       *reinterpret_cast<u32x4*>(kd + 16 * unit) = r.k[i];
@@ -329,11 +276,11 @@ struct RowState {
   float m, negm, l;
 };
 
-// K operands of one staged bf16 block: key 16h + n, dims op_dim(s, gq, 0..7).
+// K operands of one staged block: key 16h + n, dims op_dim(s, gq, 0..7).
 template <int D>
-__device__ __forceinline__ void read_k(const Stage<D, false>& st, int n, int gq,
+__device__ __forceinline__ void read_k(const Stage<D>& st, int n, int gq,
                                        u32x4 (&kop)[2][PCfg<D, false>::kSteps]) {
-  using S = Stage<D, false>;
+  using S = Stage<D>;
   const uint8_t* kbase = st.k + n * S::kKStride + 16 * gq;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -357,41 +304,12 @@ __device__ __forceinline__ void score_block(const u32x4 (&kop)[2][PCfg<D, false>
     }
 }
 
-// FP8 K operands of one staged block: lane (n, gq) takes key 16h + n's codes of the
-// head dims fp8_dim(gq, 0..31) (D = 64: 16 dims and 16 zero bytes).
-template <int D>
-__device__ __forceinline__ void read_k8(const Stage<D, true>& st, int n, int gq, i32x8 (&kop)[2]) {
-  using S = Stage<D, true>;
-  const uint8_t* kbase = st.k + n * S::kKStride + (D / 4) * gq;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + 16 * h * S::kKStride);
-    const u32x4 b = D == 128 ? *reinterpret_cast<const u32x4*>(kbase + 16 * h * S::kKStride + 16)
-                             : u32x4{0u, 0u, 0u, 0u};
-    kop[h] = i32x8{static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]),
-                   static_cast<int>(a[3]), static_cast<int>(b[0]), static_cast<int>(b[1]),
-                   static_cast<int>(b[2]), static_cast<int>(b[3])};
-  }
-}
-
-// Raw FP8 scores: the query row's two e4m3 terms against the block's codes, summed in
-// one accumulator (low term first); the products carry the row's power of two.
-template <int HPW>
-__device__ __forceinline__ void score_block8(const i32x8 (&kop)[2], const i32x8 (&qhi)[HPW],
-                                             const i32x8 (&qlo)[HPW], f32x4 (&sacc)[HPW][2]) {
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      sacc[hh][h] = mfma_fp8(kop[h], qhi[hh], mfma_fp8(kop[h], qlo[hh], f32x4{0.f, 0.f, 0.f, 0.f}));
-}
-
 // V^T operands of one staged block: dims 16bl + n, keys 4gq + 0..3 then 16 + 4gq + 0..3
 // (two transposing reads; lane (n, gq) addresses row 4gq + n / 4, dims 16bl + 4 (n % 4)).
-template <int D, bool FP8>
-__device__ __forceinline__ void read_v(const Stage<D, FP8>& st, int n, int gq,
+template <int D>
+__device__ __forceinline__ void read_v(const Stage<D>& st, int n, int gq,
                                        u32x4 (&vop)[PCfg<D, false>::kDimBlocks]) {
-  using S = Stage<D, FP8>;
+  using S = Stage<D>;
   const uint8_t* vbase = st.v + (4 * gq + (n >> 2)) * S::kVStride + 8 * (n & 3);
 #pragma unroll
   for (int bl = 0; bl < PCfg<D, false>::kDimBlocks; ++bl) {
@@ -411,7 +329,7 @@ template <int D, bool FP8, int HPW>
 __device__ __forceinline__ void softmax_args(bool diag, int j0, int pos, int gq,
                                              f32x4 (&sacc)[HPW][2],
                                              f32x4 (&acc)[HPW][PCfg<D, FP8>::kDimBlocks],
-                                             RowState (&rs)[HPW], const float (&c)[HPW][2],
+                                             RowState (&rs)[HPW], const float (&c)[2],
                                              float (&arg)[HPW][8], float (&amax)[HPW]) {
   using C = PCfg<D, FP8>;
   if (diag) {
@@ -429,7 +347,7 @@ __device__ __forceinline__ void softmax_args(bool diag, int j0, int pos, int gq,
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(sacc[hh][e >> 2][e & 3], c[hh][e >> 2], rs[hh].negm);
+    for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(sacc[hh][e >> 2][e & 3], c[e >> 2], rs[hh].negm);
     amax[hh] = max8(arg[hh]);
     raise |= amax[hh] > kRescaleSlack;
   }
@@ -441,8 +359,8 @@ __device__ __forceinline__ void softmax_args(bool diag, int j0, int pos, int gq,
 #pragma unroll
       for (int e = 0; e < 8; ++e) raw[e] = sacc[hh][e >> 2][e & 3];
       // The row's block maximum in log2 units (c > 0 in both halves).
-      const float mc = group_max(fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])) * c[hh][0],
-                                       fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])) * c[hh][1]));
+      const float mc = group_max(fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])) * c[0],
+                                       fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])) * c[1]));
       // Lanes whose row keeps its maximum multiply by 1 (no divergent branch, so the
       // accumulators are scaled in place).
       const bool up = mc > rs[hh].m + kRescaleSlack;  // the same in the row's four lanes
@@ -453,7 +371,7 @@ __device__ __forceinline__ void softmax_args(bool diag, int j0, int pos, int gq,
       rs[hh].m = up ? mc : rs[hh].m;
       rs[hh].negm = up ? -mc : rs[hh].negm;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(raw[e], c[hh][e >> 2], rs[hh].negm);
+      for (int e = 0; e < 8; ++e) arg[hh][e] = fmaf(raw[e], c[e >> 2], rs[hh].negm);
       amax[hh] = max8(arg[hh]);
     }
   }
@@ -522,7 +440,7 @@ void prefill_kernel(const PrefillParams p) {
   using W = WaveCfg<GWI>;
   constexpr int HPW = W::kHeadsPerWave;
   constexpr int NT = W::kThreads;
-  __shared__ Stage<D, FP8> stage[3];
+  __shared__ Stage<D> stage[3];
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slice = wid & 3, head_pair = wid >> 2;
@@ -563,50 +481,18 @@ void prefill_kernel(const PrefillParams p) {
   const unsigned qflip = qk_log2 < 0.f ? 0x80008000u : 0u;
   qk_log2 = fabsf(qk_log2);
 
-  // Q^T fragments (B operand): query token t, dims op_dim(s, gq, 0..7) as bf16; for
-  // FP8 K, dims fp8_dim(gq, 0..31) as two e4m3fn terms with the row's power of two qmul.
-  u32x4 qf[FP8 ? 1 : HPW][C::kSteps];
-  i32x8 qhi[FP8 ? HPW : 1], qlo[FP8 ? HPW : 1];
-  float qmul[HPW];
+  // Q^T fragments (B operand): query token t, dims op_dim(s, gq, 0..7).
+  u32x4 qf[HPW][C::kSteps];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const uint16_t* qrow = p.q + (static_cast<int64_t>(q0 + (valid ? t : 0)) * p.num_q_heads + h0 + hh) * D;
-    qmul[hh] = 1.f;
-    if constexpr (FP8) {
-      constexpr int NV = D / 4;  // values of the row in this lane
-      float x[NV];
 #pragma unroll
-      for (int u = 0; u < NV / 8; ++u) {
-        u32x4 w = valid ? *reinterpret_cast<const u32x4*>(qrow + fp8_dim<D>(gq, 8 * u)) : u32x4{0u, 0u, 0u, 0u};
-        w ^= u32x4{qflip, qflip, qflip, qflip};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[8 * u + 2 * k] = bf16_lo(w[k]);
-          x[8 * u + 2 * k + 1] = bf16_hi(w[k]);
-        }
-      }
-      qmul[hh] = q_to_fp8<NV>(x, qhi[hh], qlo[hh]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        qf[hh][s] = valid ? *reinterpret_cast<const u32x4*>(qrow + op_dim(s, gq, 0))
-                          : u32x4{0u, 0u, 0u, 0u};
-        qf[hh][s] ^= u32x4{qflip, qflip, qflip, qflip};
-      }
+    for (int s = 0; s < C::kSteps; ++s) {
+      qf[hh][s] = valid ? *reinterpret_cast<const u32x4*>(qrow + op_dim(s, gq, 0))
+                        : u32x4{0u, 0u, 0u, 0u};
+      qf[hh][s] ^= u32x4{qflip, qflip, qflip, qflip};
     }
   }
-  // Raw scores of a staged block.
-  auto scores = [&](const Stage<D, FP8>& st, f32x4 (&sc)[HPW][2]) {
-    if constexpr (FP8) {
-      i32x8 kop[2];
-      read_k8<D>(st, n, gq, kop);
-      score_block8<HPW>(kop, qhi, qlo, sc);
-    } else {
-      u32x4 kop[2][C::kSteps];
-      read_k<D>(st, n, gq, kop);
-      score_block<D, HPW>(kop, qf, sc);
-    }
-  };
 
   f32x4 acc[HPW][C::kDimBlocks];
   RowState rs[HPW];
@@ -638,7 +524,11 @@ void prefill_kernel(const PrefillParams p) {
   }
   __syncthreads();
   f32x4 sacc[HPW][2] = {};
-  if (wave_blocks > 0) scores(stage[0], sacc);
+  if (wave_blocks > 0) {
+    u32x4 kop[2][C::kSteps];
+    read_k<D>(stage[0], n, gq, kop);
+    score_block<D, HPW>(kop, qf, sacc);
+  }
   // FP8 page scales of the block being computed, one per 16-key half (a half lies in
   // one page; the two may differ when pages are shorter than 32 keys or not aligned to
   // blocks), and the physical pages of the next block's halves.
@@ -705,12 +595,8 @@ void prefill_kernel(const PrefillParams p) {
       // With one scale lookup per block the second half takes the first half's scales.
       const float ksc1 = scale_halves == 2 ? ksc[1] : ksc[0];
       const float vs[2] = {vsc[0], scale_halves == 2 ? vsc[1] : vsc[0]};
-      float c[HPW][2];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        c[hh][0] = fmaxf(qk_log2 * ksc[0] * qmul[hh], 1.17549435e-38f);
-        c[hh][1] = fmaxf(qk_log2 * ksc1 * qmul[hh], 1.17549435e-38f);
-      }
+      const float c[2] = {fmaxf(qk_log2 * ksc[0], 1.17549435e-38f),
+                          fmaxf(qk_log2 * ksc1, 1.17549435e-38f)};
       float pv[HPW][8];
       u32x4 ph[HPW];
       bool low;
@@ -719,9 +605,13 @@ void prefill_kernel(const PrefillParams p) {
       softmax_args<D, FP8, HPW>(diag, j0, pos, gq, sacc, acc, rs, c, arg, amax);
       // The next block's scores, issued among this block's exponentials (unused after
       // the wave's last block, whose next buffer then holds an earlier block).
-      scores(stage[nxt], sacc);
+      {
+        u32x4 kop[2][C::kSteps];
+        read_k<D>(stage[nxt], n, gq, kop);
+        score_block<D, HPW>(kop, qf, sacc);
+      }
       softmax_probs<FP8, HPW>(arg, amax, rs, vs, pv, ph, low);
-      read_v<D, FP8>(stage[cur], n, gq, vop);
+      read_v<D>(stage[cur], n, gq, vop);
       pv_block<D, HPW>(vop, pv, ph, low, acc);
     }
 #pragma unroll
