@@ -26,8 +26,10 @@ lengths differ. The pages give no cost, order or tie rule; the readings here:
   It equals the total when enough workers stay busy to the end and grows with the
   tail the busiest workers leave. WORKER_RATIO (how many workers saturate the chip)
   and ITEM_BYTES (the fixed cost of one work item in chip-wide bytes, ~2.6 us at
-  ~6.5 TB/s) were measured on MI355X. The last term is the partials written and read
-  back by the combine.
+  ~6.5 TB/s) come from measurements on MI355X and are kept as a pair: together they
+  pick the fastest measured power-of-two tile on every benchmark workload, although
+  one eight-wave workgroup alone streams at about chip / 240 rather than chip / 160.
+  The last term is the partials written and read back by the combine.
 
 This is the plain definition (a full sort and a heap over every item); the native
 planner uses an equivalent faster form and must match it bit for bit.
