@@ -66,6 +66,7 @@ struct PlanLds {
   u32 rkey[kMaxDevicePlanBatch];        // remainder-tile keys ((T - c) << 13 | b), sorted
   int32_t fbx[kMaxDevicePlanBatch];     // exclusive prefix of full items (x Hkv)
   int32_t rtb[kMaxDevicePlanBatch];     // exclusive prefix of n_b
+  int32_t len[kMaxDevicePlanBatch];     // seq_lens, read from global memory once
   u32 xbuf[2][NT];                      // exchange buffers of the register sort
   int32_t wcnt[kMaxDevicePlanWorkers];  // remainder items per worker
   int32_t woff[kMaxDevicePlanWorkers];  // first item of each worker
@@ -237,32 +238,6 @@ __device__ void block_scan5(const long long (&a)[5], long long (&pre)[2], long l
   __syncthreads();
 }
 
-// Exclusive prefix sum of v (thread order); *total = workgroup sum. Waves from
-// `nact` threads on hold zeros.
-template <int NT>
-__device__ long long block_scan(long long v, int nact, PlanLds<NT>& sm, long long* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  long long inc = v;
-  if (wid * 64 < nact) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-  }
-  if (lane == 63) sm.red[0][wid] = inc;
-  __syncthreads();
-  long long base = 0, t = 0;
-  for (int w = 0; w < NT / 64; ++w) {
-    const long long s = sm.red[0][w];
-    base += (w < wid) ? s : 0;
-    t += s;
-  }
-  __syncthreads();
-  *total = t;
-  return base + inc - v;
-}
-
 // Workgroup maximum of v >= 0; waves from `nact` threads on hold zeros.
 template <int NT>
 __device__ long long block_max(long long v, int nact, PlanLds<NT>& sm) {
@@ -340,6 +315,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
   long long a[5] = {0, 0, 0, 0, 0};  // tiles, full tiles, tokens, bad lengths, remainders
   for (int b = b0; b < b1; ++b) {
     const int L = p.seq_lens[b];
+    sm.len[b] = L;  // read back by this thread below, by all after the barriers
     if (L < minL) {
       a[3] = 1;
       continue;
@@ -370,7 +346,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
   {
     int pn = static_cast<int>(pre[0]), pf = static_cast<int>(pre[1]);
     for (int b = b0; b < b1; ++b) {
-      const unsigned L = static_cast<unsigned>(p.seq_lens[b]);
+      const unsigned L = static_cast<unsigned>(sm.len[b]);
       const unsigned f = L / uT;
       const unsigned c = L - f * uT;
       sm.rtb[b] = pn;
@@ -421,7 +397,10 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
     }
     if (tid == 0) sm.first_miss = lim;
     const u32 below = block_exclusive_min(raised, lim, sm);
-    if (tid < lim && key > below) atomicMin(&sm.first_miss, tid);
+    // The first item that breaks the batch: each wave's first failing lane, found by a
+    // ballot, so at most one LDS atomic per wave.
+    const unsigned long long fails = __builtin_amdgcn_ballot_w64(tid < lim && key > below);
+    if (fails != 0 && (tid & 63) == 0) atomicMin(&sm.first_miss, (tid & ~63) + __builtin_ctzll(fails));
     __syncthreads();
     const int np = sm.first_miss;
     if (tid < np) {
@@ -442,23 +421,25 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
 
   // Estimate: fluid over the sorted loads (summation-by-parts form), most items on a
   // worker, partial bytes.
-  long long term = 0, items_w = 0;
+  // Thread t holds the t-th smallest load here, and worker t's item count (cnt, whose
+  // exclusive prefix is worker t's first item in the list).
+  long long term = 0, cnt = 0;
   if (tid < W) {
     const long long l = ref + static_cast<long long>(key >> kWorkerBits);
     term = (tid <= W - 1 - kWorkerRatio ? l : 0) + (tid == W - 1 ? kWorkerRatio * l : 0);
-    items_w = base + (tid < r ? 1 : 0) + sm.wcnt[tid];
+    cnt = base + (tid < r ? 1 : 0) + sm.wcnt[tid];
   }
-  long long fluid;
-  block_scan(term, W, sm, &fluid);
-  const long long max_items = block_max(items_w, W, sm);
+  long long wpre[2], wtot[5];
+  {
+    const long long a[5] = {cnt, 0, term, 0, 0};
+    block_scan5(a, wpre, wtot, W, sm);
+  }
+  const long long off = wpre[0], total = wtot[0], fluid = wtot[2];
+  const long long max_items = block_max(cnt, W, sm);
   *est = p.kv_bytes_per_token * fluid + max_items * kItemBytes +
          N * p.rows * (p.head_dim + 1) * 8;
 
   // 4. Worker offsets, then the items.
-  long long cnt = 0;
-  if (tid < W) cnt = base + (tid < r ? 1 : 0) + sm.wcnt[tid];
-  long long total;
-  const long long off = block_scan(cnt, W, sm, &total);
   if (tid < W) {
     sm.woff[tid] = static_cast<int>(off);
     o.worker_offsets[tid] = static_cast<int>(off);
@@ -467,26 +448,28 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
   __syncthreads();
 
   int4* items = reinterpret_cast<int4*>(o.items);
-  // Full items: the x-th goes to worker x mod W at position x / W.
-  const int nF = static_cast<int>(F);
-  for (int x = tid; x < nF; x += NT) {
-    int lo = 0, hi = B - 1;  // last b with fbx[b] <= x
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.fbx[mid] <= x)
-        lo = mid;
-      else
-        hi = mid - 1;
+  // Full items: the x-th in (b, g, i) order goes to worker x mod W at position x / W.
+  // One (request, kv head) pair per thread and step: its f items are x0 .. x0 + f - 1
+  // with x0 = fbx[b] + g f, so the worker and position advance without a division.
+  if (F > 0) {
+    for (int pq = tid; pq < B * Hkv; pq += NT) {
+      const int b = pq / Hkv, g = pq - b * Hkv;
+      const unsigned L = static_cast<unsigned>(sm.len[b]);
+      const int f = static_cast<int>(L / uT);
+      if (f == 0) continue;
+      const int n = f + (L - static_cast<unsigned>(f) * uT != 0 ? 1 : 0);
+      const int x0 = sm.fbx[b] + g * f;
+      int pos = x0 / W;
+      int w = x0 - pos * W;
+      const int slot0 = Hkv * sm.rtb[b] + g * n;
+      for (int i = 0; i < f; ++i) {
+        items[sm.woff[w] + pos] = make_int4(b, g, i, slot0 + i);
+        if (++w == W) {
+          w = 0;
+          ++pos;
+        }
+      }
     }
-    const int b = lo;
-    const unsigned L = static_cast<unsigned>(p.seq_lens[b]);
-    const int f = static_cast<int>(L / uT);
-    const int n = f + (L - static_cast<unsigned>(f) * uT != 0 ? 1 : 0);
-    const int within = x - sm.fbx[b];
-    const int g = within / f;
-    const int i = within - g * f;
-    const int w = x % W;
-    items[sm.woff[w] + x / W] = make_int4(b, g, i, Hkv * sm.rtb[b] + g * n + i);
   }
   // Remainder items, in placement order after the worker's full items. The
   // placements were written by this workgroup before the barriers above.
@@ -495,7 +478,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
     const int qv = x / Hkv;
     const int g = x - qv * Hkv;
     const int b = static_cast<int>(sm.rkey[qv] & ((1u << kReqBits) - 1));
-    const int i = static_cast<int>(static_cast<unsigned>(p.seq_lens[b]) / uT);
+    const int i = static_cast<int>(static_cast<unsigned>(sm.len[b]) / uT);
     const int2 asg = o.assign[x];
     const int fw = static_cast<int>(base) + (asg.x < r ? 1 : 0);
     items[sm.woff[asg.x] + fw + asg.y] = make_int4(b, g, i, Hkv * sm.rtb[b] + g * (i + 1) + i);
