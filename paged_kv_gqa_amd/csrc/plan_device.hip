@@ -134,7 +134,7 @@ __device__ __forceinline__ unsigned lane_xor(unsigned v, int j, int lane) {
 template <int N, int NT>
 __device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds<NT>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const bool active = __builtin_amdgcn_readfirstlane(tid) < N;  // wave-uniform
+  const bool active = N >= NT || __builtin_amdgcn_readfirstlane(tid) < N;  // wave-uniform
   int buf = 0;
 #pragma unroll
   for (int k = 2; k <= N; k <<= 1) {
@@ -155,9 +155,10 @@ __device__ __forceinline__ u32 sort_keys_n(u32 x, PlanLds<NT>& sm) {
   return x;
 }
 
-// sort_keys_n for a power of two n <= NT known at run time.
+// sort_keys_n for a power of two n <= NT known at run time (the request keys, once per
+// plan; kept out of line, one copy of the ten networks).
 template <int NT>
-__device__ u32 sort_keys(u32 x, int n, PlanLds<NT>& sm) {
+__device__ __attribute__((noinline)) u32 sort_keys(u32 x, int n, PlanLds<NT>& sm) {
   switch (n) {
     case 1: return x;
     case 2: return sort_keys_n<2>(x, sm);
@@ -373,7 +374,6 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
   // load relative to ref = base * T.
   const long long base = F / W;
   const int r = static_cast<int>(F - base * W);
-  const int nW = pow2_at_least(W);
   long long ref = base * T;
   u32 key = ~0u;
   if (tid < W) {
@@ -409,7 +409,9 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
       sm.wcnt[w] += 1;
       key = raised;
     }
-    key = sort_keys(key, nW, sm);
+    // All NT keys are sorted (threads from W on hold the ~0u sentinel, above every
+    // key), so the network is fixed at compile time and inlined.
+    key = sort_keys_n<NT, NT>(key, sm);
     if (tid == 0) sm.kmin = key;
     __syncthreads();
     // Re-base the relative loads on the new least load (every key is at least kmin).
