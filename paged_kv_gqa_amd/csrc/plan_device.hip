@@ -464,6 +464,7 @@ __device__ int build_plan(const DevicePlanParams& p, long long T, PlanLds<NT>& s
       int pos = x0 / W;
       int w = x0 - pos * W;
       const int slot0 = Hkv * sm.rtb[b] + g * n;
+#pragma unroll 4
       for (int i = 0; i < f; ++i) {
         items[sm.woff[w] + pos] = make_int4(b, g, i, slot0 + i);
         if (++w == W) {
