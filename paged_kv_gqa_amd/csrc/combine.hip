@@ -5,8 +5,9 @@
 // parallel, one split per lane: lane i reads lse_i, the wave takes the maximum and
 // each lane forms w_i = exp(lse_i - max). The partial outputs are then accumulated
 // in split order with the weights broadcast from their lanes; their loads do not
-// depend on each other, so several are in flight at once. Fixed summation order
-// keeps the result deterministic. A request with a single tile is copied (its partial
+// depend on each other, so several are in flight at once (rows of at most 16 splits
+// load them together with the lse values). Fixed summation order keeps the result
+// deterministic. A request with a single tile is copied (its partial
 // is already normalised: the output is cast to bf16, the lse passed through).
 #include "kernels.hpp"
 
@@ -22,6 +23,7 @@ constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kRowsPerBlock = 4;
 constexpr int kUnroll = 8;
+constexpr int kDirect = 16;  // rows of at most this many splits load all partials at once
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -70,6 +72,49 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(const Combi
       orow[lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[0]));
     }
     if (p.lse_out != nullptr && lane == 0) p.lse_out[orow_idx] = lse[0];
+    return;
+  }
+
+  if (nb <= kDirect) {  // the outputs load with the lse values
+    float ov[kDirect][E];
+#pragma unroll
+    for (int u = 0; u < kDirect; ++u) {
+      if (u < nb) {
+        const float* src = o + u * ostride;
+        if constexpr (E == 2) {
+          const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+          ov[u][0] = v[0];
+          ov[u][1] = v[1];
+        } else {
+          ov[u][0] = *src;
+        }
+      }
+    }
+    const float l = (lane < nb) ? lse[static_cast<int64_t>(lane) * p.rows] : -INFINITY;
+    const float mx = wave_max(l) * kLog2e;
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    const float wl = (lane < nb) ? __builtin_amdgcn_exp2f(l * kLog2e - m_use) : 0.f;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kDirect; ++u) {
+      if (u < nb) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += w * ov[u][e];
+      }
+    }
+    const float den = wave_sum(wl);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    if constexpr (E == 2) {
+      f32x2 v = {acc[0] * inv, acc[1] * inv};
+      *reinterpret_cast<bf16x2*>(orow + 2 * lane) = __builtin_convertvector(v, bf16x2);
+    } else {
+      orow[lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[0] * inv));
+    }
+    if (p.lse_out != nullptr && lane == 0)
+      p.lse_out[orow_idx] = den > 0.f ? (m_use + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
     return;
   }
 
