@@ -256,27 +256,23 @@ __device__ long long block_max(long long v, int nact, PlanLds<NT>& sm) {
 }
 
 // Exclusive prefix minimum of v over threads 0 .. n-1 (thread order; ~0 for thread
-// 0 and for threads >= n).
+// 0 and for threads >= n). Within a wave, a butterfly over the lane-exchange pattern of
+// the sort (no LDS): at level j each lane takes its partner block's minimum, which
+// counts towards the lane's prefix when the partner block lies below it (lane & j).
 template <int NT>
 __device__ u32 block_exclusive_min(u32 v, int n, PlanLds<NT>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const bool active = wid * 64 < n;
-  u32 inc = tid < n ? v : ~0u;
-  if (active) {
+  u32 total = tid < n ? v : ~0u, excl = ~0u;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const u32 y = __shfl_up(inc, o);
-      if (lane >= o) inc = umin(inc, y);
-    }
+  for (int j = 1; j < 64; j <<= 1) {
+    const u32 other = lane_xor(total, j, lane);
+    if (lane & j) excl = umin(excl, other);
+    total = umin(total, other);
   }
-  if (lane == 63) sm.wmin[wid] = inc;
+  if (lane == 0) sm.wmin[wid] = total;  // the wave's minimum, in every lane
   __syncthreads();
-  u32 pre = ~0u;
+  u32 pre = excl;
   for (int w = 0; w < wid; ++w) pre = umin(pre, sm.wmin[w]);
-  if (active) {
-    const u32 prev = __shfl_up(inc, 1);
-    if (lane > 0) pre = umin(pre, prev);
-  }
   return tid < n ? pre : ~0u;
 }
 
