@@ -149,3 +149,28 @@ def test_mixed_batches_are_few_and_large():
         ref = oracle_plan.lpt_plan(sl, cfg["num_kv_heads"], T, 256)
         assert np.array_equal(items, ref["items"])
         assert batches <= 6
+
+
+def wave_exclusive_min(values):
+    """The kernel's in-wave butterfly: at level j each lane takes its partner block's
+    minimum (lane ^ j), which joins the lane's prefix when that block lies below it."""
+    total = list(values)
+    excl = [0xFFFFFFFF] * 64
+    j = 1
+    while j < 64:
+        other = [total[lane ^ j] for lane in range(64)]
+        excl = [min(e, o) if lane & j else e for lane, (e, o) in enumerate(zip(excl, other))]
+        total = [min(t, o) for t, o in zip(total, other)]
+        j *= 2
+    return excl, total
+
+
+def test_wave_butterfly_is_the_exclusive_prefix_minimum():
+    rng = np.random.default_rng(7)
+    for _ in range(500):
+        v = [int(x) for x in rng.integers(0, 1 << 31, 64)]
+        for lane in rng.integers(0, 64, int(rng.integers(0, 20))):
+            v[lane] = 0xFFFFFFFF          # lanes past the batch hold the sentinel
+        excl, total = wave_exclusive_min(v)
+        assert excl == [min(v[:lane], default=0xFFFFFFFF) for lane in range(64)]
+        assert total == [min(v)] * 64
