@@ -22,7 +22,8 @@ REQ_BITS = 13     # request index in the low bits of a remainder key
 
 
 def device_model(seq_lens, Hkv, T, W):
-    """(items [N, 4], worker_offsets [W + 1], loads [W], number of batches)."""
+    """(items [N, 4], worker_offsets [W + 1], loads [W] by worker, number of batches,
+    loads sorted ascending)."""
     L = np.asarray(seq_lens, dtype=np.int64)
     B = len(L)
     f = L // T
